@@ -1,0 +1,8 @@
+"""Fused exact-attention forward for AMD MI355X (gfx950).
+
+The compute path is a HIP library, ``libexattn.so``, behind a C ABI
+(``include/exattn.h``). This package holds its sources (``csrc/``), the build
+step and a thin ctypes binding with the same entry-point names. Importing the
+package does not load the library; the first call does, and fails loudly when
+the library has not been built.
+"""
