@@ -1,0 +1,204 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single]
+
+A step is one pass of the hot path over one batch of synthetic input that is
+already resident in HBM. For the default workload (B=4, H=16, N=2048, d=128,
+bfloat16) a step is one non-causal and one causal attn_fwd call. The line
+printed is the whole-job throughput in TFLOP/s, counting 4*B*H*N^2*d flops per
+non-causal call (2*B*H*N_q*N_kv*(d_qk+d_v) in general) and half that for a
+causal one.
+
+Alongside it:
+  * roofline: the dominant kernel's algorithmic flops per launch divided by its
+    average launch duration, timed with HIP events on the stream it runs on,
+    against the dense bf16 MFMA peak; traffic is the HBM bytes per launch from
+    the committed rocprofv3 counter summary when it was taken on the current
+    kernel source, else null;
+  * cpu_baseline: the float64 CPU oracle timed on this host's cores over a
+    bounded sample of the same workload (run before the GPU is touched, since
+    its worker pool forks).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "device.h", "launch.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary."""
+    path = os.path.join(PROFILES, f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w_list, max_heads: int):
+    """Time the oracle (as it stands) on up to max_heads heads of each workload."""
+    import oracle
+    from exact_attention_81_amd import synth
+
+    procs = max(1, min(16, os.cpu_count() or 1))
+    flops = 0.0
+    t0 = time.perf_counter()
+    parts = []
+    for w in w_list:
+        q, k, v = synth.qkv_for(w)
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+        oracle.attention_parallel(q, k, v, w.scale, w.causal, processes=procs, heads=heads)
+        flops += w.flops() * len(heads) / (w.B * w.H)
+        parts.append(f"{len(heads)} of {w.B * w.H} heads of {w.label()}")
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
+            "sample": "; ".join(parts) + f" ({dt:.1f} s wall, float64 numpy, fork pool)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="single",
+                    choices=["single", "tiny", "asym", "sweep512", "sweep1024", "sweep2048",
+                             "sweep4096", "sweep8192", "sweep16384"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
+              f"forward is sharded by (batch, head) with no communication, so N GPUs would each "
+              f"run this same one-GPU workload.", file=sys.stderr)
+        sys.exit(2)
+
+    from exact_attention_81_amd import synth
+
+    if args.workload.startswith("sweep"):
+        n = int(args.workload[5:])
+        ws = [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
+    elif args.workload in ("tiny", "asym"):
+        ws = [synth.workload(args.workload)]
+    else:
+        ws = [synth.workload("single", causal=c) for c in (False, True)]
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(ws, args.cpu_heads)
+
+    import torch
+
+    import exact_attention_81_amd as ea
+
+    dev = torch.device("cuda:0")
+    inputs = []
+    for w in ws:
+        q, k, v = synth.qkv_for(w)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty((w.B, w.H, w.N_q, w.d_v), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+        inputs.append((w, q, k, v, o, lse))
+
+    def step(events=None):
+        for i, (w, q, k, v, o, lse) in enumerate(inputs):
+            if events is not None:
+                events[i][0].record()
+            ea.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in inputs] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(w.flops() for w in ws)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per = []
+    for i, (w, *_rest) in enumerate(inputs):
+        durs = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
+        avg_ms = sum(durs) / len(durs)
+        per.append({"variant": w.label(), "avg_launch_us": avg_ms * 1e3,
+                    "tflops": w.flops() / (avg_ms * 1e-3) / 1e12,
+                    "min_launch_us": min(durs) * 1e3})
+    for p in per:
+        p["pct_of_peak"] = 100.0 * p["tflops"] / PEAK["bf16"]
+    dom = max(range(len(per)), key=lambda i: per[i]["avg_launch_us"])
+    achieved = per[dom]["tflops"]
+    traffic = committed_traffic(args.workload)
+
+    w0 = ws[0]
+    line = {
+        "metric": "attention fwd TFLOP/s (4BHN^2d, causal halved) + % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q,K,V ~ N(0,1) rounded to bf16, seeded torch CPU generator",
+        "pct_of_peak": round(100.0 * value / PEAK["bf16"], 2),
+        "config": {
+            "workload": " + ".join(w.label() for w in ws),
+            "B": w0.B, "H": w0.H, "N_q": w0.N_q, "N_kv": w0.N_kv, "d_qk": w0.d_qk,
+            "d_v": w0.d_v, "causal": [w.causal for w in ws],
+            "step": "one attn_fwd call per listed variant",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"attn_fwd_kernel ({per[dom]['variant']})",
+            "achieved": round(achieved, 2),
+            "peak": PEAK["bf16"],
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK["bf16"], 4),
+            "traffic": traffic,
+        },
+        "per_variant": per,
+        "wall_s_timed_region": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

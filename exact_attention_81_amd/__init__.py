@@ -6,3 +6,13 @@ step and a thin ctypes binding with the same entry-point names. Importing the
 package does not load the library; the first call does, and fails loudly when
 the library has not been built.
 """
+from .binding import (  # noqa: F401
+    AttnError,
+    attn_fwd,
+    attn_fwd_fp8,
+    attn_fwd_tau,
+    attn_quantize_fp8,
+    attn_strerror,
+    library_path,
+    load_library,
+)

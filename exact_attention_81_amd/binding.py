@@ -1,0 +1,178 @@
+"""ctypes binding of libexattn.so: argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, checks the
+things ctypes cannot (device, dtype, contiguity), allocates the outputs with
+``torch.empty`` and calls the C entry point of the same name on torch's current
+stream. All arithmetic happens in the HIP kernels; there is no fallback. A
+missing library raises an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libexattn.so"
+
+ATTN_BF16 = 0
+ATTN_FP16 = 1
+FP8_BLOCK = 128
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero return code of the C ABI."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {attn_strerror(code)} (code {code})")
+
+
+def library_path() -> str:
+    return os.path.join(PKG, LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree libexattn.so and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -m exact_attention_81_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_tau.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    lib.attn_fwd_tau.restype = i
+    lib.attn_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp]
+    lib.attn_quantize_fp8.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_strerror.argtypes = [i]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(t, name, dtypes):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (BHND)")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _fwd(q, k, v, causal, scale, tau, out, lse):
+    import torch
+
+    _check(q, "q", (torch.bfloat16, torch.float16))
+    _check(k, "k", (q.dtype,))
+    _check(v, "v", (q.dtype,))
+    B, H, n_q, d_qk = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, n_kv, d_qk) or v.shape != (B, H, n_kv, d_v):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = d_qk ** -0.5
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
+    lib = load_library()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_kv, d_qk, d_v,
+            float(scale), int(bool(causal)), dtype]
+    if tau is None:
+        rc = lib.attn_fwd(*args, _stream(q))
+        where = "attn_fwd"
+    else:
+        rc = lib.attn_fwd_tau(*args, int(tau), _stream(q))
+        where = "attn_fwd_tau"
+    if rc != 0:
+        raise AttnError(rc, where)
+    return out, lse
+
+
+def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+             out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """O [B,H,N_q,d_v] (dtype of q) and LSE [B,H,N_q] float32."""
+    return _fwd(q, k, v, causal, scale, None, out, lse)
+
+
+def attn_fwd_tau(q, k, v, *, tau: int, causal: bool = False, scale: Optional[float] = None,
+                 out=None, lse=None):
+    """attn_fwd with the rescale threshold tau (0 or 8, in doublings)."""
+    return _fwd(q, k, v, causal, scale, tau, out, lse)
+
+
+def attn_quantize_fp8(x, *, signs=None, transpose: bool = False):
+    """e4m3 codes (uint8) and per-128-token float32 descales of a bf16 [B,H,N,d] tensor."""
+    import torch
+
+    _check(x, "x", (torch.bfloat16,))
+    B, H, N, d = x.shape
+    nb = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    shape = (B, H, d, N) if transpose else (B, H, N, d)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    desc = torch.empty((B, H, nb), dtype=torch.float32, device=x.device)
+    if signs is not None:
+        if not signs.is_cuda or signs.dtype != torch.float32 or signs.numel() != d:
+            raise ValueError("signs must be a float32 GPU tensor of d elements")
+        signs = signs.contiguous()
+    rc = load_library().attn_quantize_fp8(_ptr(x), _ptr(x8), _ptr(desc), B, H, N, d, _ptr(signs),
+                                          int(bool(transpose)), _stream(x))
+    if rc != 0:
+        raise AttnError(rc, "attn_quantize_fp8")
+    return x8, desc
+
+
+def attn_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, *, causal: bool = False,
+                 scale: Optional[float] = None, out=None, lse=None):
+    """Attention on e4m3 codes; v8t is [B,H,d_v,N_kv]. Returns bf16 O and float32 LSE."""
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8t", v8t)):
+        _check(t, name, (torch.uint8,))
+    B, H, n_q, d_qk = q8.shape
+    n_kv = k8.shape[2]
+    d_v = v8t.shape[2]
+    if k8.shape != (B, H, n_kv, d_qk) or v8t.shape != (B, H, d_v, n_kv):
+        raise ValueError("shape mismatch between q8, k8 and v8t")
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if scale is None:
+        scale = d_qk ** -0.5
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q8.device)
+    rc = load_library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_descale),
+                                     _ptr(k_descale), _ptr(v_descale), _ptr(out), _ptr(lse),
+                                     B, H, n_q, n_kv, d_qk, d_v, float(scale), int(bool(causal)),
+                                     _stream(q8))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_fp8")
+    return out, lse

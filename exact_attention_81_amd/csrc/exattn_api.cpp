@@ -1,0 +1,146 @@
+// C ABI of libexattn.so: argument validation and dispatch to the gfx950 kernels.
+// The contract of every entry point is documented in include/exattn.h.
+#include "exattn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+using exattn::FwdParams;
+
+constexpr int64_t kMaxElems = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool too_big(int64_t a, int64_t b, int64_t c, int64_t d) {
+  // a*b*c*d >= 2^31, evaluated without overflow (all factors >= 1).
+  int64_t x = a * b;
+  if (x >= kMaxElems) return true;
+  x *= c;
+  if (x >= kMaxElems) return true;
+  return x * d >= kMaxElems;
+}
+
+bool supported_dims16(int d_qk, int d_v) {
+  return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
+}
+
+int check_shape(int B, int H, int N_q, int N_kv, int d_qk, int d_v) {
+  if (B < 1 || H < 1 || N_q < 1 || N_kv < 1) return ATTN_ERR_SHAPE;
+  if (too_big(B, H, N_q, d_qk) || too_big(B, H, N_kv, d_qk) || too_big(B, H, N_kv, d_v) ||
+      too_big(B, H, N_q, d_v))
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+int check_scale(float scale) {
+  return (std::isfinite(scale) && scale >= 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
+}
+
+int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
+          int N_kv, int d_qk, int d_v, float scale, int causal, int dtype, int tau, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (int rc = check_shape(B, H, N_q, N_kv, d_qk, d_v)) return rc;
+  if (!supported_dims16(d_qk, d_v)) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if (tau != 0 && tau != 8) return ATTN_ERR_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  FwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = exattn::launch_fwd16(p, d_qk, d_v, causal != 0, dtype == ATTN_FP16, tau,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N_q, int N_kv, int d_qk, int d_v, float scale, int causal, int dtype,
+             void* stream) {
+  return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, 8, stream);
+}
+
+int attn_fwd_tau(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N_q, int N_kv, int d_qk, int d_v, float scale, int causal, int dtype,
+                 int tau_log2, void* stream) {
+  return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, tau_log2,
+               stream);
+}
+
+int attn_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B, int H, int N, int d,
+                      const float* signs, int transpose_out, void* stream) {
+  if (!x || !x8 || !descale) return ATTN_ERR_NULL;
+  if (check_shape(B, H, N, N, d, d)) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(descale)) return ATTN_ERR_ALIGN;
+  if (signs && !aligned16(signs)) return ATTN_ERR_ALIGN;
+  if (transpose_out != 0 && transpose_out != 1) return ATTN_ERR_ARG;
+  if (transpose_out && (N % 16) != 0) return ATTN_ERR_SHAPE;
+  hipError_t e = exattn::launch_quantize_fp8(x, x8, descale, B, H, N, signs, transpose_out != 0,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const float* q_descale,
+                 const float* k_descale, const float* v_descale, void* o, float* lse, int B, int H,
+                 int N_q, int N_kv, int d_qk, int d_v, float scale, int causal, void* stream) {
+  if (!q8 || !k8 || !v8t || !q_descale || !k_descale || !v_descale || !o || !lse)
+    return ATTN_ERR_NULL;
+  if (int rc = check_shape(B, H, N_q, N_kv, d_qk, d_v)) return rc;
+  if (d_qk != 128 || d_v != 128) return ATTN_ERR_HEADDIM;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if ((N_kv % 16) != 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  FwdParams p = {};
+  p.q = q8;
+  p.k = k8;
+  p.v = v8t;
+  p.o = o;
+  p.lse = lse;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  p.B = B;
+  p.H = H;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = exattn::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (a size < 1, a tensor with >= 2^31 elements, or N not a multiple of 16 where required)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimensions";
+    case ATTN_ERR_DTYPE: return "unsupported dtype";
+    case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    case ATTN_ERR_ARG: return "argument out of range";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+/*
+ * exattn.h - C ABI of libexattn.so, the fused exact-attention forward for
+ * AMD MI355X (gfx950).
+ *
+ * The operation: for every batch b and head h,
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,   LSE = logsumexp rows,
+ * computed without materialising the N_q x N_kv score matrix: query tiles are
+ * kept on chip while key/value tiles stream through, and an online softmax
+ * keeps a running row maximum and a running row sum, rescales the accumulator
+ * and divides once at the end ("Attention at Scale - From FlashAttention to
+ * FlashAttention-4", sections "The Problem" and "The Evolution"; "FlashAttention
+ * 3 and 4: When the Bottleneck Moves", sections 2.1 and 3.2).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
+ *     the comment says otherwise. Tensors are dense, contiguous, row-major
+ *     [B, H, N, d] ("BHND"): element (b, h, n, c) sits at ((b*H + h)*N + n)*d + c.
+ *   - The caller owns every buffer. The library never allocates, frees or
+ *     synchronises; it keeps no mutable global state, so calls are reentrant.
+ *     Inputs are read-only; outputs must not alias inputs.
+ *   - Calls are asynchronous: they validate the arguments, enqueue kernels on
+ *     `stream` (a hipStream_t; NULL = the null stream) and return. A fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - Every entry point returns ATTN_OK (0) or a negative error code, checked
+ *     in this order: null pointer, shape, head dims, dtype, scale, alignment,
+ *     then the launch itself (ATTN_ERR_HIP). On an error nothing is enqueued.
+ *   - Inputs holding Inf or NaN propagate NaN into the affected rows; they are
+ *     not trapped.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V and O for attn_fwd. */
+enum {
+    ATTN_BF16 = 0, /* bfloat16 */
+    ATTN_FP16 = 1  /* IEEE half */
+};
+
+/* Return codes. */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,    /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,   /* B, H, N_q or N_kv < 1, or a tensor has >= 2^31 elements */
+    ATTN_ERR_HEADDIM = -3, /* (d_qk, d_v) not one of (64,64), (128,128), (192,128);
+                              for the fp8 entry points only (128,128) */
+    ATTN_ERR_DTYPE = -4,   /* dtype is neither ATTN_BF16 nor ATTN_FP16 */
+    ATTN_ERR_SCALE = -5,   /* scale is negative, NaN or infinite */
+    ATTN_ERR_ALIGN = -6,   /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_HIP = -7,     /* the kernel launch failed (hipGetLastError) */
+    ATTN_ERR_ARG = -8      /* another argument is out of range (tau, transpose flag) */
+};
+
+/*
+ * attn_fwd - fused attention forward, 16-bit inputs.
+ *
+ *   q    [B, H, N_q,  d_qk]  dtype    queries
+ *   k    [B, H, N_kv, d_qk]  dtype    keys
+ *   v    [B, H, N_kv, d_v ]  dtype    values
+ *   o    [B, H, N_q,  d_v ]  dtype    output, fully written (rounded to nearest even)
+ *   lse  [B, H, N_q]         float32  natural-log logsumexp of the scaled scores,
+ *                                     ln(sum_j exp(scale * q_i . k_j)) over visible j;
+ *                                     fully written
+ *   scale   softmax scale, finite and >= 0 (usually 1/sqrt(d_qk))
+ *   causal  0: every key is visible. 1: key j is visible to query i iff
+ *           j <= i + (N_kv - N_q) (bottom-right aligned; the lower triangle
+ *           when N_q == N_kv). A query with no visible key gets O = 0 and
+ *           LSE = -inf.
+ *   dtype   ATTN_BF16 or ATTN_FP16
+ *
+ * Products run on bf16/fp16 MFMA with fp32 accumulation; softmax statistics
+ * are fp32. The row maximum used for the exponentials is refreshed only when
+ * it has grown by more than 8 doublings (a factor 256), as in "FlashAttention
+ * 3 and 4: When the Bottleneck Moves", section 3.2; the result is the same
+ * softmax since every row is divided by its own final sum.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N_q, int N_kv, int d_qk, int d_v,
+             float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_fwd_tau - attn_fwd with an explicit rescale threshold, for checking
+ * that the conditional rescale leaves the result unchanged.
+ *   tau_log2  0: refresh the row maximum whenever it grows (plain online
+ *             softmax); 8: the attn_fwd behaviour. Other values: ATTN_ERR_ARG.
+ */
+int attn_fwd_tau(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N_q, int N_kv, int d_qk, int d_v,
+                 float scale, int causal, int dtype, int tau_log2, void* stream);
+
+/*
+ * attn_quantize_fp8 - per-block fp8 (OCP e4m3) quantisation, with an optional
+ * random-sign Hadamard rotation ("FlashAttention 3 and 4: When the Bottleneck
+ * Moves", section 2.2: one scale per block of values; Q and K multiplied by a
+ * fixed random rotation, which cancels in Q K^T).
+ *
+ *   x        [B, H, N, d] bfloat16 input
+ *   x8       uint8 e4m3 codes: [B, H, N, d], or [B, H, d, N] when transpose_out = 1
+ *   descale  [B, H, ceil(N/128)] float32: a block is 128 consecutive tokens x d
+ *   signs    device pointer to d floats, each +1 or -1 (any value >= 0 counts as
+ *            +1, any value < 0 as -1), or NULL for no rotation. With signs the block is rotated by
+ *            R = diag(signs) H_d / sqrt(d) (H_d the Sylvester Hadamard matrix).
+ *   d        must be 128
+ *   transpose_out  0 or 1 (1 is the layout attn_fwd_fp8 takes for V)
+ *
+ * Arithmetic (bit-exact by construction): y = x diag(signs) H_d is summed in
+ * float64 (exact for bfloat16 inputs); amax = max|y| over the block;
+ * code = e4m3_rne_saturating(float32(y * (448 / amax))) with the product and
+ * quotient in float64; descale = float32(amax / (448 * sqrt(d))) with signs,
+ * float32(amax / 448) without. An all-zero block gets codes 0 and descale 0.
+ * Dequantised values code * descale approximate x R (or x).
+ */
+int attn_quantize_fp8(const void* x, uint8_t* x8, float* descale,
+                      int B, int H, int N, int d, const float* signs,
+                      int transpose_out, void* stream);
+
+/*
+ * attn_fwd_fp8 - fused attention forward on fp8 e4m3 inputs made by
+ * attn_quantize_fp8 (Q and K with the same signs, V with transpose_out = 1).
+ *
+ *   q8 [B,H,N_q,d_qk], k8 [B,H,N_kv,d_qk], v8t [B,H,d_v,N_kv]  uint8 e4m3 codes
+ *   q_descale [B,H,ceil(N_q/128)], k_descale, v_descale [B,H,ceil(N_kv/128)]  float32
+ *   o [B,H,N_q,d_v] bfloat16, lse [B,H,N_q] float32: as for attn_fwd
+ *   d_qk = d_v = 128.
+ *
+ * Both products run on the fp8 MFMA (e4m3 x e4m3 -> fp32); the softmax
+ * weights are rounded to e4m3 for the second product.
+ */
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                 const float* q_descale, const float* k_descale, const float* v_descale,
+                 void* o, float* lse, int B, int H, int N_q, int N_kv, int d_qk, int d_v,
+                 float scale, int causal, void* stream);
+
+/* Static, NUL-terminated description of a return code (never NULL). */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

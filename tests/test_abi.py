@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments with the documented codes before touching a GPU.
+
+Only argument combinations that fail validation are passed: validation runs on
+the host and returns before any HIP call, so no kernel is launched here. The
+pointers are fake (never dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_81_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exattn.h")
+
+P = 4096  # a fake, 16-byte aligned "device" address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"(ATTN_\w+)\s*=\s*(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ea.library_path()):
+        pytest.skip("libexattn.so not built")
+    return ea.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == ["attn_fwd", "attn_fwd_fp8", "attn_fwd_tau", "attn_quantize_fp8", "attn_strerror"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_covers_codes(lib):
+    c = codes()
+    for name, val in c.items():
+        if name.startswith("ATTN_ERR") or name == "ATTN_OK":
+            s = ea.attn_strerror(val)
+            assert s and s != "unknown error code", name
+    assert ea.attn_strerror(12345) == "unknown error code"
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nkv=8, dqk=128, dv=128, scale=0.1,
+             causal=0, dtype=0)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                        a["Nkv"], a["dqk"], a["dv"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def test_attn_fwd_validation(lib):
+    c = codes()
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: None}) == c["ATTN_ERR_NULL"]
+    for name in ("B", "H", "Nq", "Nkv"):
+        assert fwd(lib, **{name: 0}) == c["ATTN_ERR_SHAPE"]
+        assert fwd(lib, **{name: -3}) == c["ATTN_ERR_SHAPE"]
+    assert fwd(lib, B=1 << 12, H=1 << 12, Nq=128) == c["ATTN_ERR_SHAPE"]   # 2^31 elements
+    assert fwd(lib, B=1 << 15, H=1 << 15, Nq=1 << 15) == c["ATTN_ERR_SHAPE"]  # no overflow
+    for dqk, dv in ((96, 96), (128, 64), (192, 192), (64, 128), (256, 256)):
+        assert fwd(lib, dqk=dqk, dv=dv) == c["ATTN_ERR_HEADDIM"]
+    assert fwd(lib, dtype=2) == c["ATTN_ERR_DTYPE"]
+    assert fwd(lib, dtype=-1) == c["ATTN_ERR_DTYPE"]
+    for s in (math.nan, math.inf, -math.inf, -0.5):
+        assert fwd(lib, scale=s) == c["ATTN_ERR_SCALE"]
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: P + 8}) == c["ATTN_ERR_ALIGN"]
+    assert fwd(lib, causal=2) == c["ATTN_ERR_ARG"]
+    # precedence: null beats shape beats head dims beats dtype beats scale beats alignment
+    assert fwd(lib, q=None, B=0) == c["ATTN_ERR_NULL"]
+    assert fwd(lib, B=0, dqk=96) == c["ATTN_ERR_SHAPE"]
+    assert fwd(lib, dqk=96, dtype=7) == c["ATTN_ERR_HEADDIM"]
+    assert fwd(lib, dtype=7, scale=math.nan) == c["ATTN_ERR_DTYPE"]
+    assert fwd(lib, scale=math.nan, q=P + 2) == c["ATTN_ERR_SCALE"]
+
+
+def test_attn_fwd_tau_validation(lib):
+    c = codes()
+    rc = lib.attn_fwd_tau(P, P, P, P, P, 1, 1, 8, 8, 128, 128, 0.1, 0, 0, 3, None)
+    assert rc == c["ATTN_ERR_ARG"]
+    rc = lib.attn_fwd_tau(None, P, P, P, P, 1, 1, 8, 8, 128, 128, 0.1, 0, 0, 8, None)
+    assert rc == c["ATTN_ERR_NULL"]
+
+
+def test_quantize_validation(lib):
+    c = codes()
+    q = lib.attn_quantize_fp8
+    assert q(None, P, P, 1, 1, 128, 128, None, 0, None) == c["ATTN_ERR_NULL"]
+    assert q(P, P, P, 0, 1, 128, 128, None, 0, None) == c["ATTN_ERR_SHAPE"]
+    assert q(P, P, P, 1, 1, 128, 64, None, 0, None) == c["ATTN_ERR_HEADDIM"]
+    assert q(P, P + 4, P, 1, 1, 128, 128, None, 0, None) == c["ATTN_ERR_ALIGN"]
+    assert q(P, P, P, 1, 1, 128, 128, P + 4, 0, None) == c["ATTN_ERR_ALIGN"]
+    assert q(P, P, P, 1, 1, 128, 128, None, 2, None) == c["ATTN_ERR_ARG"]
+    assert q(P, P, P, 1, 1, 100, 128, None, 1, None) == c["ATTN_ERR_SHAPE"]
+
+
+def test_fwd_fp8_validation(lib):
+    c = codes()
+    f = lib.attn_fwd_fp8
+    base = [P, P, P, P, P, P, P, P, 1, 1, 128, 128, 128, 128, 0.1, 0, None]
+    for i in range(8):
+        a = list(base)
+        a[i] = None
+        assert f(*a) == c["ATTN_ERR_NULL"]
+    a = list(base); a[12] = 64
+    assert f(*a) == c["ATTN_ERR_HEADDIM"]
+    a = list(base); a[14] = math.nan
+    assert f(*a) == c["ATTN_ERR_SCALE"]
+    a = list(base); a[0] = P + 1
+    assert f(*a) == c["ATTN_ERR_ALIGN"]
+    a = list(base); a[11] = 100
+    assert f(*a) == c["ATTN_ERR_SHAPE"]
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, q, q)
