@@ -31,7 +31,8 @@ class AttnError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(PKG, LIB_NAME)
+    """The in-tree library, or the file named by EXATTN_LIBRARY (another build of it)."""
+    return os.environ.get("EXATTN_LIBRARY") or os.path.join(PKG, LIB_NAME)
 
 
 def load_library() -> ctypes.CDLL:

@@ -26,7 +26,8 @@ ARCH = "gfx950"
 HIP_SOURCES = ["attn_fwd.hip", "attn_fp8.hip"]
 HOST_SOURCES = ["exattn_api.cpp"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",
+          "-Wno-inline-asm"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
@@ -62,7 +63,7 @@ def build(verbose: bool = False) -> str:
                   os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
         tmp_out = os.path.join(tmp, LIB_NAME)
-        _run([cc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_out])
+        _run([cc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-o", tmp_out])
         shutil.copyfile(tmp_out, out + ".tmp")
         os.replace(out + ".tmp", out)
     if verbose:

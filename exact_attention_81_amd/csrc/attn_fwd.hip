@@ -2,23 +2,42 @@
 //
 // O = softmax(scale * Q K^T [+ causal mask]) V and LSE, one workgroup per
 // (query tile, head, batch). The query tile stays in registers while K/V tiles
-// stream from HBM through a double-buffered LDS ring; an online softmax keeps
-// a running row maximum and row sum, so the N_q x N_kv scores never leave the
-// chip ("Attention at Scale - From FlashAttention to FlashAttention-4",
-// section "The Evolution": tiling and the online softmax). Loads of tile j+1
-// are issued before the products of tile j, the gfx950 form of overlapping
-// data movement with compute ("FlashAttention 3 and 4: When the Bottleneck
-// Moves", section 2.1). The row maximum used by the exponentials is refreshed
-// only when it grows by more than TAU doublings (same page, section 3.2).
+// stream from HBM through LDS rings; an online softmax keeps a running row
+// maximum and row sum, so the N_q x N_kv scores never leave the chip
+// ("Attention at Scale - From FlashAttention to FlashAttention-4", section
+// "The Evolution": tiling and the online softmax). Tiles go straight from
+// global memory into LDS (buffer_load_dwordx4 ... lds) two iterations ahead of
+// their use, and each barrier waits only for the loads that are due, the
+// gfx950 form of overlapping data movement with compute ("FlashAttention 3
+// and 4: When the Bottleneck Moves", section 2.1). The row
+// maximum used by the exponentials is refreshed only when it grows by more
+// than TAU doublings (same page, section 3.2).
 //
-// Work split. 4 waves x 64 query rows = BLOCK_M 256 rows per workgroup; key
-// tiles of BLOCK_N 64. Each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_{bf16,f16}: the 32x32 accumulator gives every lane one
-// query column and 16 keys, so the softmax row reductions are in-lane plus one
-// exchange with lane ^ 32. The same registers, rounded to 16 bits, are the
-// B operand of O^T += V^T P^T: the key order inside an MFMA K-step is the
-// accumulator's row order, and V is written to LDS transposed with the
-// matching key permutation, so P never moves between lanes.
+// Work split and overlap. 8 waves, two per SIMD, each owning 32 query rows
+// (BLOCK_M 256); key tiles of BLOCK_N 64. Every wave runs the same sequence
+//     S(0) sm(0) | PV(0) S(1) | sm(1) | PV(1) S(2) | sm(2) ... sm(n-1) PV(n-1)
+// (S = K Q^T and PV = V^T P^T on the matrix cores, sm = softmax on the vector
+// ALU), with one workgroup barrier per key tile. Waves 0-3 (group A) meet the
+// barrier between sm(j-1) and their matrix block [PV(j-1) S(j)], waves 4-7
+// (group B) before sm(j-1). A SIMD hosts one wave of each group, so after
+// every barrier one of its waves feeds the matrix core while the other runs
+// the exponentials: the pages' "two tiles, two engines" overlap (section
+// 2.1), arranged by the barrier placement instead of warp specialisation.
+//
+// Products. S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: the 32x32
+// accumulator gives every lane one query column and 16 keys, so the softmax
+// row reductions are in-lane plus one exchange with lane ^ 32. The same
+// registers, rounded to 16 bits, are the B operand of O^T += V^T P^T; the key
+// order inside an MFMA K-step is the accumulator's row order, and the V^T
+// operand is gathered in exactly that order by ds_read_b64_tr_b16 from the
+// row-major V tile, so P never moves between lanes.
+//
+// LDS layout. K and V tiles are stored row-major with their 16-byte chunks
+// XOR-swizzled per row, which keeps both the direct-to-LDS writes (1 KB of
+// consecutive LDS per wave instruction) and the MFMA operand reads free of
+// bank conflicts.
+#include <type_traits>
+
 #include "device.h"
 
 namespace exattn {
@@ -26,11 +45,9 @@ namespace {
 
 constexpr int BLOCK_M = 256;
 constexpr int BLOCK_N = 64;
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int ROWS_PER_WAVE = BLOCK_M / NWAVES;  // 64 = two 32-query MFMA columns
-constexpr int KPAD = 8;                          // 16-byte row pad: conflict-free b128 reads
-constexpr int VPAD = 8;
+constexpr int ROWS_PER_WAVE = BLOCK_M / NWAVES;  // 32: one MFMA column block
 
 template <bool F16> struct Elem;
 template <> struct Elem<false> {
@@ -54,38 +71,106 @@ template <> struct Elem<true> {
   }
 };
 
-// Position of key `kk` (0..BLOCK_N-1) inside a row of the transposed V tile.
-// Within each group of 16 keys, bits 2 and 3 of the key index are swapped, so
-// that lanes 0-31 of an MFMA K-step find their 8 keys {0-3, 8-11} and lanes
-// 32-63 theirs {4-7, 12-15} as one contiguous 16-byte read. This is exactly
-// the key order of the S^T accumulator rows held by the two lane halves.
-__device__ constexpr int vt_pos(int kk) {
-  return (kk & ~15) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2) | (kk & 3);
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource word 3 for raw 32-bit-format buffers on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format.
+__device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return (i32x4_t){(int)(unsigned)a, (int)((a >> 32) & 0xffffu), bytes, kBufferFlags};
 }
+
+// 16 bytes per lane from `rsrc` at byte offset `voff` into LDS at dst + 16 * lane
+// (buffer_load_dwordx4 ... lds, LDS base in m0); offsets at or past the resource
+// size read as 0. Written as inline assembly so that the compiler does not track
+// these LDS writes: it would otherwise wait for every one of them (vmcnt(0))
+// before each ds_read_b64_tr_b16, which defeats loading tiles ahead. The waves
+// wait for them explicitly in tile_barrier. No other code in these kernels uses m0.
+__device__ inline void buffer_load_lds16(i32x4_t rsrc, lds_u8* dst, int voff) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding and
+// its LDS operations are done, then meet the other waves. Unlike __syncthreads
+// this leaves the newest N tile loads in flight.
+template <int N>
+__device__ inline void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ inline u32x4_t lds_read128(const lds_u8* p) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)p;
+}
+// Transposing read: within each group of 16 lanes, lane i receives element i%4
+// of the 8 bytes read by lanes 4t + i/4, t = 0..3 (a 4 x 16 block of 16-bit
+// values, returned column-wise).
+__device__ inline u32x2_t lds_read_tr16(const lds_u8* p) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Swizzled chunk position inside an LDS row of 16 chunks (256 B) or 8 chunks
+// (128 B). `w16` selects the row width.
+//   K rows, 16 chunks: chunk c of row r at c ^ (r & 15).
+//   K rows,  8 chunks: chunk c of row r at c ^ ((r >> 1) & 7).
+//   V rows, 16 chunks: chunk c of row r at c ^ (4 * (r & 3)).
+//   V rows,  8 chunks: chunk c of row r at c ^ (4 * ((r >> 1) & 1)).
+__device__ constexpr int k_swz(int c, int r, bool w16) { return w16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)); }
+__device__ constexpr int v_swz(int c, int r, bool w16) { return w16 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1))); }
 
 template <int DQK, int DV, bool CAUSAL, int TAU, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdParams p) {
-  static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
+  static_assert(DQK == 64 || DQK == 128 || DQK == 192, "d_qk");
+  static_assert(DV == 64 || DV == 128, "d_v");
   typedef Elem<F16> E;
-  constexpr int KS = DQK / 16;            // MFMA K-steps of S^T
-  constexpr int DB = DV / 32;             // 32-row blocks of O^T
-  constexpr int KROW = DQK + KPAD;        // LDS row length of K (elements)
-  constexpr int VROW = BLOCK_N + VPAD;    // LDS row length of V^T
-  constexpr int K_CHUNKS = BLOCK_N * DQK / 8;         // 16-byte chunks per K tile
-  constexpr int K_LOADS = (K_CHUNKS + NTHREADS - 1) / NTHREADS;
-  constexpr int V_UNITS = (BLOCK_N / 4) * (DV / 8);   // 4 keys x 8 columns per unit
-  constexpr int V_LOADS = (V_UNITS + NTHREADS - 1) / NTHREADS;
+  constexpr int KS = DQK / 16;             // MFMA K-steps of S^T
+  constexpr int DB = DV / 32;              // 32-row blocks of O^T
+  // K tile: part A holds dims [0, min(DQK,128)), part B (DQK = 192) dims [128, 192).
+  constexpr int KA_D = DQK > 128 ? 128 : DQK;
+  constexpr int KB_D = DQK - KA_D;
+  constexpr bool KA_W16 = KA_D == 128;
+  constexpr int KA_ROW = KA_D * 2;         // bytes
+  constexpr int KB_ROW = 128;
+  constexpr int KA_BYTES = BLOCK_N * KA_ROW;
+  constexpr int KB_BYTES = BLOCK_N * KB_D * 2;
+  constexpr int K_STAGE = KA_BYTES + KB_BYTES;
+  constexpr bool V_W16 = DV == 128;
+  constexpr int V_ROW = DV * 2;
+  constexpr int V_STAGE = BLOCK_N * V_ROW;
+  constexpr int KA_INSTR = KA_BYTES / 1024;  // wave-wide 1 KB direct loads per tile
+  constexpr int KB_INSTR = KB_BYTES / 1024;
+  constexpr int V_INSTR = V_STAGE / 1024;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BLOCK_N * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DV * VROW];
+  // Three-stage rings: iteration j reads K(j) and V(j-1) while K(j+1), V(j) (issued
+  // one iteration earlier) and K(j+2), V(j+1) (issued after its barrier) land.
+  constexpr int NSTAGE = 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (K_STAGE + V_STAGE)];
+  lds_u8* const k_lds = (lds_u8*)smem;
+  lds_u8* const v_lds = (lds_u8*)smem + NSTAGE * K_STAGE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const bool group_b = wave >= NWAVES / 2;
 
   const int BH = p.B * p.H;
   int bh, qt;
@@ -93,249 +178,318 @@ void attn_fwd_kernel(const FwdParams p) {
   const int q0 = qt * BLOCK_M;
   const int offset = p.Nkv - p.Nq;  // causal: key j visible to query i iff j <= i + offset
 
-  const uint16_t* __restrict__ qg = (const uint16_t*)p.q + (size_t)bh * p.Nq * DQK;
-  const uint16_t* __restrict__ kg = (const uint16_t*)p.k + (size_t)bh * p.Nkv * DQK;
-  const uint16_t* __restrict__ vg = (const uint16_t*)p.v + (size_t)bh * p.Nkv * DV;
+  const uint8_t* __restrict__ qg = (const uint8_t*)p.q + (size_t)bh * p.Nq * DQK * 2;
+  const uint8_t* __restrict__ kg = (const uint8_t*)p.k + (size_t)bh * p.Nkv * DQK * 2;
+  const uint8_t* __restrict__ vg = (const uint8_t*)p.v + (size_t)bh * p.Nkv * DV * 2;
 
-  // Keys this workgroup needs: all of them, or up to the last query's limit.
   int kv_end = p.Nkv;
   if (CAUSAL) kv_end = min(p.Nkv, max(0, q0 + BLOCK_M + offset));
   const int ntiles = (kv_end + BLOCK_N - 1) / BLOCK_N;
 
-  // ---- Q^T fragments (B operand): lane = query column, 8 consecutive dims.
-  const int wq0 = q0 + wave * ROWS_PER_WAVE;  // first query row of this wave
-  u32x4_t qf[2][KS];
+  // ---- Q^T fragments (B operand of S^T): lane = query column, 8 consecutive dims.
+  const int wq0 = q0 + wave * ROWS_PER_WAVE;
+  const int my_q = wq0 + l32;
+  u32x4_t qf[KS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = wq0 + qb * 32 + l32;
+  for (int s = 0; s < KS; ++s) {
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (my_q < p.Nq) x = *(const u32x4_t*)(qg + (size_t)my_q * DQK * 2 + s * 32 + half * 16);
+    qf[s] = x;
+  }
+
+  // ---- Direct-to-LDS tile loads. Wave instruction i fills LDS bytes [1024 i, 1024 i + 1024)
+  // of a ring stage; lane l writes the 16 bytes at 1024 i + 16 l, so each lane loads the
+  // global chunk that belongs at that swizzled position. The buffer resource of a tile
+  // starts at its first key and ends at N_kv: rows past the end read as zeros. Per-lane
+  // offsets do not depend on the tile.
+  static_assert(KA_INSTR % NWAVES == 0 && KB_INSTR % NWAVES == 0 && V_INSTR % NWAVES == 0,
+                "every wave issues the same number of tile loads");
+  constexpr int KA_PER = KA_INSTR / NWAVES;
+  constexpr int KB_PER = KB_INSTR / NWAVES;
+  constexpr int V_PER = V_INSTR / NWAVES;
+  constexpr int LOADS_PER_TILE = KA_PER + KB_PER + V_PER;  // per thread: K(j) + V(j - 1)
+  int ka_off[KA_PER], kb_off[KB_PER > 0 ? KB_PER : 1], v_off[V_PER];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row < p.Nq) x = *(const u32x4_t*)(qg + (size_t)row * DQK + s * 16 + half * 8);
-      qf[qb][s] = x;
+  for (int t = 0; t < KA_PER; ++t) {
+    constexpr int rows_per = 1024 / KA_ROW, cpr = KA_ROW / 16;
+    const int i = wave + t * NWAVES;
+    const int r = i * rows_per + lane / cpr;
+    ka_off[t] = r * DQK * 2 + k_swz(lane % cpr, r, KA_W16) * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < KB_PER; ++t) {
+    const int i = wave + t * NWAVES;
+    const int r = i * 8 + lane / 8;
+    kb_off[t] = r * DQK * 2 + KA_ROW + k_swz(lane % 8, r, false) * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < V_PER; ++t) {
+    constexpr int rows_per = 1024 / V_ROW, cpr = V_ROW / 16;
+    const int i = wave + t * NWAVES;
+    const int r = i * rows_per + lane / cpr;
+    v_off[t] = r * V_ROW + v_swz(lane % cpr, r, V_W16) * 16;
+  }
+  // Tiles past the last one are still "loaded" through an empty resource (every lane
+  // reads zero bytes), which keeps the number of loads in flight the same at every
+  // barrier; the stages they fill are not read again.
+  // `stage` is an int or a std::integral_constant; with the latter every LDS address
+  // below is a per-lane register plus an immediate offset.
+  auto issue_k = [&](int j, auto stage) {
+    const int key0 = min(j * BLOCK_N, p.Nkv);
+    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * DQK * 2, (p.Nkv - key0) * DQK * 2);
+    lds_u8* st = k_lds + int(stage) * K_STAGE;
+#pragma unroll
+    for (int t = 0; t < KA_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, ka_off[t]);
+#pragma unroll
+    for (int t = 0; t < KB_PER; ++t)
+      buffer_load_lds16(rs, st + KA_BYTES + (wave + t * NWAVES) * 1024, kb_off[t]);
+  };
+  auto issue_v = [&](int j, auto stage) {
+    const int key0 = min(j * BLOCK_N, p.Nkv);
+    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * DV * 2, (p.Nkv - key0) * DV * 2);
+    lds_u8* st = v_lds + int(stage) * V_STAGE;
+#pragma unroll
+    for (int t = 0; t < V_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, v_off[t]);
+  };
+
+  // ---- Per-lane LDS read offsets within a stage.
+  // K operand of S^T: lane reads row 32 kb + l32, chunk 2 s + half.
+  int koff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int c = 2 * s + half;
+    if (c < KA_D / 8) {
+      koff[s] = l32 * KA_ROW + k_swz(c, l32, KA_W16) * 16;
+    } else {
+      koff[s] = KA_BYTES + l32 * KB_ROW + k_swz(c - KA_D / 8, l32, false) * 16;
+    }
+  }
+  // V^T operand of O^T: for 16-key step ks and half h8 (keys +0 / +8), lane j of its
+  // 16-lane group reads row 16 ks + 8 h8 + 4 half + j/4, columns 32 db + 16 g16 + 4 (j%4).
+  int voff[DB];
+  {
+    const int j = lane & 15, g16 = (lane >> 4) & 1;
+    const int rl = 4 * half + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * g16 + ((j & 3) >> 1);
+      // Absolute LDS address of the lane's chunk in stage 0, kept opaque to the compiler:
+      // folded into the immediate offset of each read, the V ring base (past the K ring)
+      // plus a stage offset would exceed the 16-bit field and cost an add per read.
+      voff[db] = (int)(unsigned)(uintptr_t)v_lds + rl * V_ROW + v_swz(c, rl, V_W16) * 16 + 8 * (j & 1);
+      asm volatile("" : "+v"(voff[db]));
     }
   }
 
-  // ---- Tile staging through registers.
-  u32x4_t kreg[K_LOADS];
-  u32x4_t vreg[V_LOADS][4];
-  auto load_tile = [&](int j) {
-    const int key0 = j * BLOCK_N;
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = i * NTHREADS + tid;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (c < K_CHUNKS) {
-        const int r = c / (DQK / 8), col = c % (DQK / 8);
-        if (key0 + r < p.Nkv) x = *(const u32x4_t*)(kg + (size_t)(key0 + r) * DQK + col * 8);
-      }
-      kreg[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int u = i * NTHREADS + tid;
-      const int kq = u % (BLOCK_N / 4), oct = u / (BLOCK_N / 4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        const int key = key0 + kq * 4 + t;
-        if (u < V_UNITS && key < p.Nkv) x = *(const u32x4_t*)(vg + (size_t)key * DV + oct * 8);
-        vreg[i][t] = x;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int c = i * NTHREADS + tid;
-      if (c < K_CHUNKS) {
-        const int r = c / (DQK / 8), col = c % (DQK / 8);
-        *(u32x4_t*)(&k_lds[buf][r * KROW + col * 8]) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int u = i * NTHREADS + tid;
-      if (u < V_UNITS) {
-        const int kq = u % (BLOCK_N / 4), oct = u / (BLOCK_N / 4);
-        const int pos = vt_pos(kq * 4);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned a0 = vreg[i][0][w], a1 = vreg[i][1][w];
-          const unsigned a2 = vreg[i][2][w], a3 = vreg[i][3][w];
-          // column 2w: low halves of the four keys; column 2w+1: high halves
-          u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                        __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-          u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                        __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-          *(u32x2_t*)(&v_lds[buf][(oct * 8 + 2 * w) * VROW + pos]) = lo;
-          *(u32x2_t*)(&v_lds[buf][(oct * 8 + 2 * w + 1) * VROW + pos]) = hi;
-        }
-      }
-    }
-  };
-
-  // ---- Accumulators and softmax state (per lane: 2 query columns).
-  f32x16_t oacc[DB][2];
+  f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
-  float m_ref[2] = {-INFINITY, -INFINITY};  // running max, log2 units
-  float l_part[2] = {0.f, 0.f};             // this lane's partial row sums
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  f32x16_t sacc[2];          // S^T of a tile between its S and softmax phases
+  u32x4_t pf[4];             // P^T B operands of a tile between its softmax and PV phases
+  float m_ref = -INFINITY;   // running reference max, log2 units
+  float l_part = 0.f;        // this lane's partial row sum
   const float c = p.scale_log2;
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  // S(j): S^T = K_j Q^T into sacc. Operands are read one K-step ahead of the products;
+  // the scheduling fences keep the compiler from hoisting every read above the first
+  // product (16 live fragments).
+  auto s_phase = [&](auto stage) {
+    const lds_u8* st = k_lds + int(stage) * K_STAGE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    auto kread = [&](int s_, int kb) {
+      const int rows = (2 * s_ + half < KA_D / 8) ? kb * 32 * KA_ROW : kb * 32 * KB_ROW;
+      return lds_read128(st + koff[s_] + rows);
+    };
+    u32x4_t kf0 = kread(0, 0), kf1 = kread(0, 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4_t nf0 = kf0, nf1 = kf1;
+      if (s + 1 < KS) {
+        nf0 = kread(s + 1, 0);
+        nf1 = kread(s + 1, 1);
+      }
+      sacc[0] = E::mfma(kf0, qf[s], sacc[0]);
+      sacc[1] = E::mfma(kf1, qf[s], sacc[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      kf0 = nf0;
+      kf1 = nf1;
+    }
+  };
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(j + 1);  // in flight during the products below
+  // PV(j): O^T += V_j^T P_j^T from pf, operands one step ahead as above.
+  auto pv_phase = [&](auto stage) {
+    lds_u8* const lds0 = (lds_u8*)(uintptr_t)0;  // voff holds absolute LDS addresses
+    const lds_u8* st = lds0 + int(stage) * V_STAGE;
+    auto vread = [&](int step) {
+      const int ks = step / DB, db = step % DB;
+      const lds_u8* a = st + voff[db] + ks * 16 * V_ROW;
+      const u32x2_t lo = lds_read_tr16(a);
+      const u32x2_t hi = lds_read_tr16(a + 8 * V_ROW);
+      return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4_t vf = vread(0);
+#pragma unroll
+    for (int step = 0; step < 4 * DB; ++step) {
+      u32x4_t nv = vf;
+      if (step + 1 < 4 * DB) nv = vread(step + 1);
+      oacc[step % DB] = E::mfma(vf, pf[step / DB], oacc[step % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+      vf = nv;
+    }
+  };
 
-    const int key0 = j * BLOCK_N;
-    // Skip the products when every key of the tile is in this wave's future.
-    const bool wave_active = !CAUSAL || key0 <= wq0 + ROWS_PER_WAVE - 1 + offset;
-    if (wave_active) {
-      // S^T = K Q^T: 2 key blocks x 2 query blocks of 32x32.
-      f32x16_t sacc[2][2];
+  // sm(j): masking (MASK: a key of the tile is past N_kv or past this wave's diagonal),
+  // row max, conditional rescale, exponentials, row sum; sacc -> pf.
+  auto softmax = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Row r of key block kb is key j*BLOCK_N + kb*32 + 8*(r>>2) + 4*half + (r&3); it is
+    // visible iff its tile-local offset kb*32 + 8*(r>>2) + (r&3) (a constant) is at most
+    // `room`. Comparing constants against one per-tile value keeps the mask from
+    // holding 32 per-lane offsets in registers.
+    int room = 0;
+    auto visible = [&](int kb, int r) { return kb * 32 + (r >> 2) * 8 + (r & 3) <= room; };
+    if constexpr (MASK) {
+      const int limit = CAUSAL ? min(p.Nkv - 1, my_q + offset) : p.Nkv - 1;
+      room = limit - j * BLOCK_N - half * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
-      const uint16_t* kt = &k_lds[buf][0];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4_t kf = *(const u32x4_t*)(kt + (kb * 32 + l32) * KROW + s * 16 + half * 8);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) sacc[kb][qb] = E::mfma(kf, qf[qb][s], sacc[kb][qb]);
-        }
-      }
-
-      // Mask the tail tile and the tiles that cross this wave's diagonal.
-      const bool need_mask = (key0 + BLOCK_N > p.Nkv) ||
-                             (CAUSAL && key0 + BLOCK_N - 1 > wq0 + offset);
-      unsigned vis[2][2] = {{0xffffu, 0xffffu}, {0xffffu, 0xffffu}};  // bit r: key visible
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int query = wq0 + qb * 32 + l32;
-            const int limit = CAUSAL ? min(p.Nkv - 1, query + offset) : p.Nkv - 1;
-            unsigned bits = 0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-              const bool ok = key <= limit;
-              bits |= (ok ? 1u : 0u) << r;
-              if (!ok) sacc[kb][qb][r] = -INFINITY;
-            }
-            vis[kb][qb] = bits;
-          }
-      }
-
-      // Online softmax: tile row max, conditional rescale, exponentials.
-      float m_new[2];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = sacc[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-        mx = max_halves(mx);
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-        m_new[qb] = fmaxf(m_ref[qb], mt);
-        grow |= m_new[qb] > m_ref[qb] + (float)TAU;
-      }
-      if (__any(grow)) {  // wave-uniform branch; only rows past the threshold re-base
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bool mine = m_new[qb] > m_ref[qb] + (float)TAU;
-          const float alpha = mine ? __builtin_amdgcn_exp2f(m_ref[qb] - m_new[qb]) : 1.f;
-          m_ref[qb] = mine ? m_new[qb] : m_ref[qb];
-          l_part[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
-        }
-      }
-      u32x4_t pf[2][4];  // P^T B operands: [query block][16-key step]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float nm = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float pv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], c, nm));
-            if (need_mask) e = ((vis[kb][qb] >> r) & 1u) ? e : 0.f;
-            pv[r] = e;
-            psum += e;
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            u32x4_t w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = E::pack2(pv[h * 8 + 2 * i], pv[h * 8 + 2 * i + 1]);
-            pf[qb][kb * 2 + h] = w;
-          }
-        }
-        l_part[qb] += psum;
-      }
-
-      // O^T += V^T P^T.
-      const uint16_t* vt = &v_lds[buf][0];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4_t vf = *(const u32x4_t*)(vt + (db * 32 + l32) * VROW + ks * 16 + half * 8);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = E::mfma(vf, pf[qb][ks], oacc[db][qb]);
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          if (!visible(kb, r)) sacc[kb][r] = -INFINITY;
     }
-
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
-  uint16_t* __restrict__ og = (uint16_t*)p.o + (size_t)bh * p.Nq * DV;
-  float* __restrict__ lg = p.lse + (size_t)bh * p.Nq;
+    float mx = sacc[0][0];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l = sum_halves(l_part[qb]);
-    const int row = wq0 + qb * 32 + l32;
-    const bool any = l > 0.f;
-    const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
-    if (row < p.Nq) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_halves(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const bool grow = mt > m_ref + (float)TAU;
+    if (__any(grow)) {  // wave-uniform branch; only rows past the threshold re-base
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
+      m_ref = grow ? mt : m_ref;
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2_t w = {E::pack2(oacc[db][qb][g * 4 + 0] * inv, oacc[db][qb][g * 4 + 1] * inv),
-                       E::pack2(oacc[db][qb][g * 4 + 2] * inv, oacc[db][qb][g * 4 + 3] * inv)};
-          *(u32x2_t*)(og + (size_t)row * DV + db * 32 + g * 8 + half * 4) = w;
-        }
-      if (half == 0)
-        lg[row] = any ? 0.69314718055994531f * (m_ref[qb] + __builtin_amdgcn_logf(l)) : -INFINITY;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, nm));
+        if constexpr (MASK) e = visible(kb, r) ? e : 0.f;
+        pv[r] = e;
+        psum += e;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = E::pack2(pv[h * 8 + 2 * i], pv[h * 8 + 2 * i + 1]);
+        pf[kb * 2 + h] = w;
+      }
+    }
+    l_part += psum;
+  };
+
+  // Tiles [0, j_plain) need no mask for any wave of the workgroup; a tile that starts
+  // after this wave's last visible key (causal) is skipped by the wave. For causal
+  // problems every wave still sees tile j_plain.
+  int j_plain = min(ntiles, p.Nkv / BLOCK_N);
+  if (CAUSAL) j_plain = min(j_plain, max(0, (q0 + offset + 1) / BLOCK_N));
+  const int wave_last_key = wq0 + ROWS_PER_WAVE - 1 + offset;
+  auto active = [&](int j) { return !CAUSAL || j * BLOCK_N <= wave_last_key; };
+  constexpr std::false_type PLAIN{};
+  constexpr std::true_type MASKED{};
+
+  // Barrier j needs K(j) and V(j-1) and lets the loads issued after barrier j-1, K(j+1)
+  // and V(j), stay in flight; right after it the wave issues K(j+2) and V(j+1). Every
+  // wave runs sm(j-1) PV(j-1) S(j) per iteration; group B meets barrier j before its
+  // softmax, group A after it, so group A's matrix block follows the barrier while
+  // group B computes exponentials, and the other way round before the next barrier.
+  auto barrier_and_issue = [&](int j, auto k_next, auto v_next) {
+    tile_barrier<LOADS_PER_TILE>();
+    issue_k(j + 2, k_next);
+    issue_v(j + 1, v_next);
+  };
+  // Iteration j with ring stages known at compile time, R = j % 3: K(j) in stage R,
+  // V(j-1) in stage (R+2) % 3; K(j+2) goes to stage (R+2) % 3, V(j+1) to (R+1) % 3.
+  auto plain_iter = [&](int j, auto r_tag) {
+    constexpr int R = decltype(r_tag)::value;
+    constexpr std::integral_constant<int, R> k_cur{};
+    constexpr std::integral_constant<int, (R + 2) % NSTAGE> v_prev{};
+    constexpr std::integral_constant<int, (R + 2) % NSTAGE> k_next{};
+    constexpr std::integral_constant<int, (R + 1) % NSTAGE> v_next{};
+    if (group_b) barrier_and_issue(j, k_next, v_next);
+    softmax(j - 1, PLAIN);
+    if (!group_b) barrier_and_issue(j, k_next, v_next);
+    pv_phase(v_prev);
+    s_phase(k_cur);
+  };
+  // The same with stages computed at run time (tiles that need masking, and the few
+  // iterations that do not fill a group of three).
+  auto any_iter = [&](int j) {
+    const int r = j % NSTAGE;
+    if (group_b) barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    if (active(j - 1)) {
+      if (j - 1 < j_plain) softmax(j - 1, PLAIN); else softmax(j - 1, MASKED);
+    }
+    if (!group_b) barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    if (active(j - 1)) pv_phase((r + 2) % NSTAGE);
+    if (active(j)) s_phase(r);
+  };
+  if (ntiles > 0) {
+    issue_k(0, 0);
+    issue_k(1, 1);
+    issue_v(0, 0);
+    barrier_and_issue(0, 2, 1);
+    if (active(0)) s_phase(0);
+    // Iterations j <= j_plain have a plain softmax and every wave active.
+    const int j_last_plain = min(j_plain, ntiles - 1);
+    int j = 1;
+    for (; j + 2 <= j_last_plain; j += 3) {
+      plain_iter(j, std::integral_constant<int, 1>{});
+      plain_iter(j + 1, std::integral_constant<int, 2>{});
+      plain_iter(j + 2, std::integral_constant<int, 0>{});
+    }
+    for (; j < ntiles; ++j) any_iter(j);
+    if (group_b) tile_barrier<LOADS_PER_TILE>();
+    if (active(ntiles - 1)) {
+      if (ntiles - 1 < j_plain) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
+    }
+    if (!group_b) tile_barrier<LOADS_PER_TILE>();
+    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE);
+  }
+
+  __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end
+
+  // ---- Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  const float l = sum_halves(l_part);
+  const bool any = l > 0.f;
+  const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
+  if (my_q < p.Nq) {
+    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * DV * 2;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2_t w = {E::pack2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv),
+                     E::pack2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv)};
+        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
+      }
+    if (half == 0)
+      p.lse[(size_t)bh * p.Nq + my_q] =
+          any ? 0.69314718055994531f * (m_ref + __builtin_amdgcn_logf(l)) : -INFINITY;
   }
 }
 
