@@ -321,7 +321,11 @@ void attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  // PV(j): O^T += V_j^T P_j^T from pf, operands one step ahead as above.
+  // PV(j): O^T += V_j^T P_j^T from pf. A transposing LDS read takes longer than one
+  // product, so operands are read PV_AHEAD products ahead (the S accumulators are dead
+  // here, which leaves room for the extra fragments).
+  constexpr int PV_STEPS = 4 * DB;
+  constexpr int PV_AHEAD = 3;
   auto pv_phase = [&](auto stage) {
     lds_u8* const lds0 = (lds_u8*)(uintptr_t)0;  // voff holds absolute LDS addresses
     const lds_u8* st = lds0 + int(stage) * V_STAGE;
@@ -332,14 +336,15 @@ void attn_fwd_kernel(const FwdParams p) {
       const u32x2_t hi = lds_read_tr16(a + 8 * V_ROW);
       return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
     };
-    u32x4_t vf = vread(0);
+    u32x4_t vf[PV_AHEAD];
 #pragma unroll
-    for (int step = 0; step < 4 * DB; ++step) {
-      u32x4_t nv = vf;
-      if (step + 1 < 4 * DB) nv = vread(step + 1);
-      oacc[step % DB] = E::mfma(vf, pf[step / DB], oacc[step % DB]);
+    for (int i = 0; i < PV_AHEAD; ++i) vf[i] = vread(i);
+#pragma unroll
+    for (int step = 0; step < PV_STEPS; ++step) {
+      const u32x4_t cur = vf[step % PV_AHEAD];
+      if (step + PV_AHEAD < PV_STEPS) vf[step % PV_AHEAD] = vread(step + PV_AHEAD);
+      oacc[step % DB] = E::mfma(cur, pf[step / DB], oacc[step % DB]);
       __builtin_amdgcn_sched_barrier(0);
-      vf = nv;
     }
   };
 
@@ -417,6 +422,19 @@ void attn_fwd_kernel(const FwdParams p) {
   // wave runs sm(j-1) PV(j-1) S(j) per iteration; group B meets barrier j before its
   // softmax, group A after it, so group A's matrix block follows the barrier while
   // group B computes exponentials, and the other way round before the next barrier.
+  // Compiler-only fences (no instructions): a value "modified" by an empty volatile asm
+  // must be complete before it and cannot be computed earlier than it. They pin the
+  // softmax to its side of the barrier, which the compiler would otherwise move
+  // (exponentials sunk next to the PV products, the row max hoisted above the barrier),
+  // putting both wave groups in the same phase.
+  auto pin_s = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(sacc[kb]));
+  };
+  auto pin_p = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pf[i]));
+  };
   auto barrier_and_issue = [&](int j, auto k_next, auto v_next) {
     tile_barrier<LOADS_PER_TILE>();
     issue_k(j + 2, k_next);
@@ -430,9 +448,15 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr std::integral_constant<int, (R + 2) % NSTAGE> v_prev{};
     constexpr std::integral_constant<int, (R + 2) % NSTAGE> k_next{};
     constexpr std::integral_constant<int, (R + 1) % NSTAGE> v_next{};
-    if (group_b) barrier_and_issue(j, k_next, v_next);
+    if (group_b) {
+      barrier_and_issue(j, k_next, v_next);
+      pin_s();
+    }
     softmax(j - 1, PLAIN);
-    if (!group_b) barrier_and_issue(j, k_next, v_next);
+    if (!group_b) {
+      pin_p();
+      barrier_and_issue(j, k_next, v_next);
+    }
     pv_phase(v_prev);
     s_phase(k_cur);
   };
@@ -440,11 +464,17 @@ void attn_fwd_kernel(const FwdParams p) {
   // iterations that do not fill a group of three).
   auto any_iter = [&](int j) {
     const int r = j % NSTAGE;
-    if (group_b) barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    if (group_b) {
+      barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+      pin_s();
+    }
     if (active(j - 1)) {
       if (j - 1 < j_plain) softmax(j - 1, PLAIN); else softmax(j - 1, MASKED);
     }
-    if (!group_b) barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    if (!group_b) {
+      pin_p();
+      barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    }
     if (active(j - 1)) pv_phase((r + 2) % NSTAGE);
     if (active(j)) s_phase(r);
   };
