@@ -57,24 +57,35 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w_list, max_heads: int):
-    """Time the oracle (as it stands) on up to max_heads heads of each workload."""
+def cpu_baseline(w_list, max_heads: int, min_seconds: float = 10.0):
+    """Time the oracle (as it stands) on up to max_heads heads of each workload.
+
+    The sample is repeated until at least min_seconds of wall time have passed, so
+    that small workloads are still timed over a stable interval.
+    """
     import oracle
     from exact_attention_81_amd import synth
 
     procs = max(1, min(16, os.cpu_count() or 1))
-    flops = 0.0
-    t0 = time.perf_counter()
-    parts = []
+    data = []
     for w in w_list:
-        q, k, v = synth.qkv_for(w)
         heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
-        oracle.attention_parallel(q, k, v, w.scale, w.causal, processes=procs, heads=heads)
-        flops += w.flops() * len(heads) / (w.B * w.H)
-        parts.append(f"{len(heads)} of {w.B * w.H} heads of {w.label()}")
-    dt = time.perf_counter() - t0
+        data.append((w, synth.qkv_for(w), heads))
+    flops = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for w, (q, k, v), heads in data:
+            oracle.attention_parallel(q, k, v, w.scale, w.causal, processes=procs, heads=heads)
+            flops += w.flops() * len(heads) / (w.B * w.H)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    parts = [f"{len(heads)} of {w.B * w.H} heads of {w.label()}" for w, _, heads in data]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
-            "sample": "; ".join(parts) + f" ({dt:.1f} s wall, float64 numpy, fork pool)"}
+            "sample": "; ".join(parts) + f", {reps} time(s) ({dt:.1f} s wall, float64 numpy, "
+                                        f"fork pool)"}
 
 
 def main():
@@ -87,6 +98,9 @@ def main():
                              "sweep4096", "sweep8192", "sweep16384"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, run a plain float32 copy of this many MiB "
+                         "three times (calibrates the HBM byte counters of a profiler run)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -145,6 +159,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    if args.copy_mib > 0:
+        # Reads and writes copy_mib MiB per launch; outside the timed region.
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     step_flops = sum(w.flops() for w in ws)
@@ -194,6 +217,7 @@ def main():
             "traffic": traffic,
         },
         "per_variant": per,
+        "kernel_source_sha": kernel_source_hash(),
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }

@@ -326,7 +326,7 @@ void attn_fwd_kernel(const FwdParams p) {
   // here, which leaves room for the extra fragments).
   constexpr int PV_STEPS = 4 * DB;
   constexpr int PV_AHEAD = 3;
-  auto pv_phase = [&](auto stage) {
+  auto pv_phase = [&](auto stage, auto hook) {
     lds_u8* const lds0 = (lds_u8*)(uintptr_t)0;  // voff holds absolute LDS addresses
     const lds_u8* st = lds0 + int(stage) * V_STAGE;
     auto vread = [&](int step) {
@@ -344,9 +344,11 @@ void attn_fwd_kernel(const FwdParams p) {
       const u32x4_t cur = vf[step % PV_AHEAD];
       if (step + PV_AHEAD < PV_STEPS) vf[step % PV_AHEAD] = vread(step + PV_AHEAD);
       oacc[step % DB] = E::mfma(cur, pf[step / DB], oacc[step % DB]);
+      hook(step);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto no_hook = [](int) {};
 
   // sm(j): masking (MASK: a key of the tile is past N_kv or past this wave's diagonal),
   // row max, conditional rescale, exponentials, row sum; sacc -> pf.
@@ -418,7 +420,7 @@ void attn_fwd_kernel(const FwdParams p) {
   constexpr std::true_type MASKED{};
 
   // Barrier j needs K(j) and V(j-1) and lets the loads issued after barrier j-1, K(j+1)
-  // and V(j), stay in flight; right after it the wave issues K(j+2) and V(j+1). Every
+  // and V(j), stay in flight; after it the wave issues K(j+2) and V(j+1). Every
   // wave runs sm(j-1) PV(j-1) S(j) per iteration; group B meets barrier j before its
   // softmax, group A after it, so group A's matrix block follows the barrier while
   // group B computes exponentials, and the other way round before the next barrier.
@@ -440,6 +442,33 @@ void attn_fwd_kernel(const FwdParams p) {
     issue_k(j + 2, k_next);
     issue_v(j + 1, v_next);
   };
+  // The tile loads of an unrolled iteration are spread over its PV products, one every
+  // ISSUE_GAP products, instead of all eight waves issuing theirs right after the
+  // barrier: the burst (32 KB per workgroup at d = 128) queues in the vector memory
+  // pipeline and stalls the waves behind it.
+  constexpr int ISSUE_GAP = PV_STEPS / LOADS_PER_TILE;
+  static_assert(ISSUE_GAP >= 1, "one load per PV product at most");
+  auto spread_issue = [&](int j, auto k_next, auto v_next) {
+    const int kkey0 = min((j + 2) * BLOCK_N, p.Nkv);
+    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * DQK * 2, (p.Nkv - kkey0) * DQK * 2);
+    const int vkey0 = min((j + 1) * BLOCK_N, p.Nkv);
+    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * DV * 2, (p.Nkv - vkey0) * DV * 2);
+    lds_u8* kst = k_lds + int(k_next) * K_STAGE;
+    lds_u8* vst = v_lds + int(v_next) * V_STAGE;
+    return [=](int step) {
+      if (step % ISSUE_GAP != 0) return;
+      const int li = step / ISSUE_GAP;
+      if (li < KA_PER) {
+        buffer_load_lds16(krs, kst + (wave + li * NWAVES) * 1024, ka_off[li]);
+      } else if (li < KA_PER + KB_PER) {
+        const int t = li - KA_PER;
+        buffer_load_lds16(krs, kst + KA_BYTES + (wave + t * NWAVES) * 1024, kb_off[t]);
+      } else if (li < LOADS_PER_TILE) {
+        const int t = li - KA_PER - KB_PER;
+        buffer_load_lds16(vrs, vst + (wave + t * NWAVES) * 1024, v_off[t]);
+      }
+    };
+  };
   // Iteration j with ring stages known at compile time, R = j % 3: K(j) in stage R,
   // V(j-1) in stage (R+2) % 3; K(j+2) goes to stage (R+2) % 3, V(j+1) to (R+1) % 3.
   auto plain_iter = [&](int j, auto r_tag) {
@@ -449,15 +478,15 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr std::integral_constant<int, (R + 2) % NSTAGE> k_next{};
     constexpr std::integral_constant<int, (R + 1) % NSTAGE> v_next{};
     if (group_b) {
-      barrier_and_issue(j, k_next, v_next);
+      tile_barrier<LOADS_PER_TILE>();
       pin_s();
     }
     softmax(j - 1, PLAIN);
     if (!group_b) {
       pin_p();
-      barrier_and_issue(j, k_next, v_next);
+      tile_barrier<LOADS_PER_TILE>();
     }
-    pv_phase(v_prev);
+    pv_phase(v_prev, spread_issue(j, k_next, v_next));
     s_phase(k_cur);
   };
   // The same with stages computed at run time (tiles that need masking, and the few
@@ -475,7 +504,7 @@ void attn_fwd_kernel(const FwdParams p) {
       pin_p();
       barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
     }
-    if (active(j - 1)) pv_phase((r + 2) % NSTAGE);
+    if (active(j - 1)) pv_phase((r + 2) % NSTAGE, no_hook);
     if (active(j)) s_phase(r);
   };
   if (ntiles > 0) {
@@ -498,7 +527,7 @@ void attn_fwd_kernel(const FwdParams p) {
       if (ntiles - 1 < j_plain) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
     }
     if (!group_b) tile_barrier<LOADS_PER_TILE>();
-    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE);
+    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE, no_hook);
   }
 
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end

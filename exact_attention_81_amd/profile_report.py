@@ -1,0 +1,165 @@
+"""Summarise rocprofv3 output of a bench.py run into text under profiles/.
+
+    python -m exact_attention_81_amd.profile_report --workload single \\
+        --bench-json RUN/bench.json --stats RUN/stats --fetch RUN/fetch --write RUN/write \\
+        --copy-mib 1024 --commands RUN/commands.txt
+
+Inputs are the directories rocprofv3 wrote with ``--output-format csv``:
+  * ``--stats``: a ``--kernel-trace --stats`` run (``*kernel_stats.csv``);
+  * ``--fetch`` / ``--write``: ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` runs
+    (``*counter_collection.csv``, KiB per dispatch) of ``bench.py --copy-mib M``.
+The copy kernel of those runs moves a known number of bytes; dividing that by what
+the counter reads for it gives the factor that turns the counter into bytes. The
+attention kernel's counter times that factor is its HBM traffic per launch.
+
+Writes ``profiles/attn_fwd_<workload>.md`` (figures and the commands that made
+them) and ``profiles/attn_fwd_<workload>_traffic.json`` (read by bench.py, which
+uses it only while the kernel sources hash to the recorded value).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import re
+from collections import defaultdict
+
+from . import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_RE = re.compile(r"attn_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false)>")
+
+
+def _one(pattern_dir: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(pattern_dir, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {pattern_dir}")
+    return hits[0]
+
+
+def short_name(name: str) -> str:
+    m = KERNEL_RE.search(name)
+    if m:
+        dqk, dv, causal, tau, f16 = m.groups()
+        return (f"attn_fwd_kernel d{dqk}x{dv} {'causal' if causal == 'true' else 'noncausal'} "
+                f"tau{tau} {'fp16' if f16 == 'true' else 'bf16'}")
+    if "neg" in name:
+        return "copy (torch.neg, float32)"
+    return name[:60]
+
+
+def kernel_stats(d: str):
+    rows = []
+    with open(_one(d, "kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            rows.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return rows
+
+
+def counter_per_dispatch(d: str, counter: str):
+    """Mean value of one counter per dispatch, by short kernel name."""
+    vals = defaultdict(list)
+    with open(_one(d, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def algorithmic_bytes(w) -> int:
+    """Q, K, V read once, O and LSE written once."""
+    bh = w.B * w.H
+    return 2 * bh * (w.N_q * w.d_qk + w.N_kv * w.d_qk + w.N_kv * w.d_v + w.N_q * w.d_v) + 4 * bh * w.N_q
+
+
+def workloads_of(name: str):
+    if name.startswith("sweep"):
+        n = int(name[5:])
+        return [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
+    if name in ("tiny", "asym"):
+        return [synth.workload(name)]
+    return [synth.workload("single", causal=c) for c in (False, True)]
+
+
+def variant_key(w) -> str:
+    return (f"attn_fwd_kernel d{w.d_qk}x{w.d_v} {'causal' if w.causal else 'noncausal'} tau8 bf16")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--bench-json", required=True)
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-mib", type=int, required=True)
+    ap.add_argument("--commands", required=True)
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args()
+
+    with open(args.bench_json) as fh:
+        bench = json.loads(fh.read().strip().splitlines()[-1])
+    with open(args.commands) as fh:
+        commands = fh.read().strip()
+    stats = kernel_stats(args.stats)
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    copy_name = "copy (torch.neg, float32)"
+    copy_bytes = args.copy_mib << 20
+    f_fetch = copy_bytes / (fetch[copy_name][0] * 1024.0)
+    f_write = copy_bytes / (write[copy_name][0] * 1024.0)
+
+    ws = workloads_of(args.workload)
+    ev = {p["variant"]: p for p in bench["per_variant"]}
+    traffic = {}
+    lines = [f"# attn_fwd, workload {args.workload}", "",
+             "Workload: " + " + ".join(w.label() for w in ws) + ".", "",
+             "## Commands", "", "```", commands, "```", "",
+             "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
+                     f"{r['max_us']:.2f} | {r['pct']:.2f} |")
+    lines += ["", "bench.py's HIP-event average of the same launches (the run under --stats):", "",
+              "| variant | avg us (events) | TFLOP/s |", "|---|---|---|"]
+    for p in bench["per_variant"]:
+        lines.append(f"| {p['variant']} | {p['avg_launch_us']:.2f} | {p['tflops']:.1f} |")
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Calibration: a float32 copy of {args.copy_mib} MiB reads and writes {copy_bytes} bytes; "
+              f"its FETCH_SIZE reads {fetch[copy_name][0]:.0f} KiB and WRITE_SIZE "
+              f"{write[copy_name][0]:.0f} KiB per dispatch, so bytes = KiB x {f_fetch * 1024:.1f} (fetch) "
+              f"and KiB x {f_write * 1024:.1f} (write).", "",
+              "| variant | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|"]
+    for w in ws:
+        key = variant_key(w)
+        if key not in fetch or key not in write:
+            continue
+        fb = fetch[key][0] * 1024.0 * f_fetch
+        wb = write[key][0] * 1024.0 * f_write
+        alg = algorithmic_bytes(w)
+        traffic[w.label()] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb,
+                              "algorithmic_bytes": alg}
+        lines.append(f"| {w.label()} | {fetch[key][0]:.0f} | {write[key][0]:.0f} | {fb + wb:.4g} | "
+                     f"{alg:.4g} | {(fb + wb) / alg:.3f} |")
+    lines.append("")
+    os.makedirs(args.out, exist_ok=True)
+    with open(os.path.join(args.out, f"attn_fwd_{args.workload}.md"), "w") as fh:
+        fh.write("\n".join(lines))
+    dom = bench["roofline"]["kernel"]
+    dom_variant = dom[dom.index("(") + 1:-1]
+    rec = {"workload": args.workload, "kernel_source_sha": bench["kernel_source_sha"],
+           "dominant_variant": dom_variant,
+           "hbm_bytes_per_launch": traffic.get(dom_variant, {}).get("hbm_bytes"),
+           "per_variant": traffic, "copy_factor_fetch": f_fetch, "copy_factor_write": f_write}
+    with open(os.path.join(args.out, f"attn_fwd_{args.workload}_traffic.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
