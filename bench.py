@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "device.h", "launch.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "device.h", "tile_io.h",
+                            "launch.h")]
 
 
 def kernel_source_hash() -> str:
@@ -94,8 +95,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="single",
-                    choices=["single", "tiny", "asym", "sweep512", "sweep1024", "sweep2048",
-                             "sweep4096", "sweep8192", "sweep16384"])
+                    choices=["single", "tiny", "asym", "fp8", "sweep512", "sweep1024",
+                             "sweep2048", "sweep4096", "sweep8192", "sweep16384"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -114,7 +115,7 @@ def main():
     if args.workload.startswith("sweep"):
         n = int(args.workload[5:])
         ws = [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
-    elif args.workload in ("tiny", "asym"):
+    elif args.workload in ("tiny", "asym", "fp8"):
         ws = [synth.workload(args.workload)]
     else:
         ws = [synth.workload("single", causal=c) for c in (False, True)]
@@ -126,19 +127,41 @@ def main():
     import exact_attention_81_amd as ea
 
     dev = torch.device("cuda:0")
-    inputs = []
+    fp8 = ws[0].fp8
+    prep = None
+    inputs = []  # (workload, launch) pairs; launch() enqueues one attention forward
     for w in ws:
-        q, k, v = synth.qkv_for(w)
-        q, k, v = q.to(dev), k.to(dev), v.to(dev)
         o = torch.empty((w.B, w.H, w.N_q, w.d_v), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
-        inputs.append((w, q, k, v, o, lse))
+        if fp8:
+            # Rotation and block quantisation happen once, outside the timed region;
+            # they are timed on their own below and reported as "prep".
+            signs, q, k, v = synth.fp8_inputs(w.B, w.H, w.N_q, w.d_qk, w.seed)
+            q, k, v, signs = q.to(dev), k.to(dev), v.to(dev), signs.to(dev)
+
+            def quantise(q=q, k=k, v=v, signs=signs):
+                return (ea.attn_quantize_fp8(q, signs=signs), ea.attn_quantize_fp8(k, signs=signs),
+                        ea.attn_quantize_fp8(v, transpose=True))
+
+            (q8, qd), (k8, kd), (v8, vd) = quantise()
+            prep = quantise
+
+            def launch(w=w, q8=q8, k8=k8, v8=v8, qd=qd, kd=kd, vd=vd, o=o, lse=lse):
+                ea.attn_fwd_fp8(q8, k8, v8, qd, kd, vd, causal=w.causal, scale=w.scale, out=o,
+                                lse=lse)
+        else:
+            q, k, v = synth.qkv_for(w)
+            q, k, v = q.to(dev), k.to(dev), v.to(dev)
+
+            def launch(w=w, q=q, k=k, v=v, o=o, lse=lse):
+                ea.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        inputs.append((w, launch))
 
     def step(events=None):
-        for i, (w, q, k, v, o, lse) in enumerate(inputs):
+        for i, (w, launch) in enumerate(inputs):
             if events is not None:
                 events[i][0].record()
-            ea.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+            launch()
             if events is not None:
                 events[i][1].record()
 
@@ -158,6 +181,18 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+
+    prep_us = None
+    if prep is not None:
+        for _ in range(3):
+            prep()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            prep()
+        e1.record()
+        torch.cuda.synchronize()
+        prep_us = e0.elapsed_time(e1) * 100.0  # per call, microseconds
 
     if args.copy_mib > 0:
         # Reads and writes copy_mib MiB per launch; outside the timed region.
@@ -180,8 +215,10 @@ def main():
         per.append({"variant": w.label(), "avg_launch_us": avg_ms * 1e3,
                     "tflops": w.flops() / (avg_ms * 1e-3) / 1e12,
                     "min_launch_us": min(durs) * 1e3})
+    dt = "fp8" if fp8 else "bf16"
+    peak = PEAK[dt]
     for p in per:
-        p["pct_of_peak"] = 100.0 * p["tflops"] / PEAK["bf16"]
+        p["pct_of_peak"] = 100.0 * p["tflops"] / peak
     dom = max(range(len(per)), key=lambda i: per[i]["avg_launch_us"])
     achieved = per[dom]["tflops"]
     traffic = committed_traffic(args.workload)
@@ -198,26 +235,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: Q,K,V ~ N(0,1) rounded to bf16, seeded torch CPU generator",
-        "pct_of_peak": round(100.0 * value / PEAK["bf16"], 2),
+        "dtype": "e4m3 (fp8) operands, f32 accumulation" if fp8 else "bf16",
+        "data": ("synthetic: Q,K,V ~ N(0,1) with 0.5% of coordinates x30, rounded to bf16, "
+                 "random-sign Hadamard rotation of Q and K, e4m3 per 128-token block"
+                 if fp8 else "synthetic: Q,K,V ~ N(0,1) rounded to bf16, seeded torch CPU generator"),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "config": {
             "workload": " + ".join(w.label() for w in ws),
             "B": w0.B, "H": w0.H, "N_q": w0.N_q, "N_kv": w0.N_kv, "d_qk": w0.d_qk,
             "d_v": w0.d_v, "causal": [w.causal for w in ws],
-            "step": "one attn_fwd call per listed variant",
+            "step": ("one attn_fwd_fp8 call on prepared e4m3 inputs" if fp8
+                     else "one attn_fwd call per listed variant"),
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": f"attn_fwd_kernel ({per[dom]['variant']})",
+            "kernel": f"{'attn_fwd_fp8_kernel' if fp8 else 'attn_fwd_kernel'} "
+                      f"({per[dom]['variant']})",
             "achieved": round(achieved, 2),
-            "peak": PEAK["bf16"],
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK["bf16"], 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
         "per_variant": per,
         "kernel_source_sha": kernel_source_hash(),
+        "fp8_prep_us": None if prep_us is None else round(prep_us, 2),
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }

@@ -1,5 +1,5 @@
 // fp8 (OCP e4m3) path for gfx950: per-block quantisation with an optional
-// random-sign Hadamard rotation, and the fp8 attention forward.
+// random-sign Hadamard rotation (the attention kernel is in attn_fwd_fp8.hip).
 //
 // "FlashAttention 3 and 4: When the Bottleneck Moves", section 2.2: the
 // tensor cores run FP8 at about twice the 16-bit rate; each block of values
@@ -149,10 +149,6 @@ hipError_t launch_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B
   hipLaunchKernelGGL(quantize_kernel, dim3(nb * B * H), dim3(QTHREADS), 0, stream,
                      (const uint16_t*)x, x8, descale, N, nb, signs, transpose_out ? 1 : 0, div);
   return hipGetLastError();
-}
-
-hipError_t launch_fwd_fp8(const FwdParams&, bool, hipStream_t) {
-  return hipErrorNotSupported;  // replaced by the fp8 attention kernel below once validated
 }
 
 }  // namespace exattn

@@ -1,0 +1,428 @@
+// Fused exact-attention forward for gfx950 on OCP e4m3 (fp8) operands.
+//
+// Inputs are the codes and per-block descales written by the quantiser: Q and
+// K [B,H,N,128] (optionally rotated by the same random-sign Hadamard matrix,
+// which cancels in Q K^T), V transposed [B,H,128,N_kv], and one float32 descale
+// per 128 tokens of each (b, h). Both products run on
+// v_mfma_f32_32x32x64_f8f6f4 at twice the 16-bit rate, with P itself rounded
+// to e4m3 ("FlashAttention 3 and 4: When the Bottleneck Moves", section 2.2;
+// "Attention at Scale - From FlashAttention to FlashAttention-4", section "The
+// Evolution", FlashAttention-3's FP8 path).
+//
+// The schedule is the one of the 16-bit kernel: 8 waves of 32 query rows,
+// 64-key tiles streamed into 3-stage LDS rings by direct-to-LDS loads, one
+// barrier per tile, and two wave groups half an iteration apart so that one
+// wave of every SIMD computes exponentials while the other feeds the matrix
+// core.
+//
+// Scales. A 64-key tile lies inside one 128-key descale block and a wave's 32
+// query rows inside one 128-query block, so the score of a tile is
+//     s * log2(e) = (scale * log2(e) * dq * dk) * (codes_q . codes_k),
+// one scalar per wave and tile times the MFMA result. P is taken as
+//     p = 2^(s - m_ref + PBIAS) * (dv / dv_ref),
+// where dv is the tile's V descale and dv_ref the largest V descale of the
+// head: the ratio folds V's dequantisation into the exponent (no per-tile
+// rescale of the accumulator), and O = dv_ref * acc / l at the end. The row
+// sum l adds p / (dv / dv_ref), i.e. the unrounded 2^(s - m_ref + PBIAS).
+// The running maximum m_ref is re-based when the row maximum grows by more
+// than TAU doublings (section 3.2 of the first page), so every p is at most
+// 2^(TAU + PBIAS) = 256, inside e4m3's range (448), while a row's largest
+// entries sit at 2^6 or above, far from e4m3's subnormals.
+//
+// Key order inside the PV product. Lane l of the S^T accumulator holds, for
+// query l % 32, keys 8q + 4(l/32) + (0..3) of both 32-key halves of the tile.
+// The B operand of O^T += V^T P^T needs lane half h to hold keys 32h..32h+31.
+// After packing to e4m3 (4 keys per dword) one v_permlane32_swap per dword
+// pair exchanges the halves, which leaves every lane with its 32 keys in
+// natural order; the V^T operand is then 32 contiguous bytes of a dim row.
+#include <type_traits>
+
+#include "device.h"
+#include "tile_io.h"
+
+namespace exattn {
+namespace {
+
+constexpr int F8_BLOCK_M = 256;
+constexpr int F8_BLOCK_N = 64;
+constexpr int F8_NWAVES = 8;
+constexpr int F8_NTHREADS = 64 * F8_NWAVES;
+constexpr int F8_ROWS = F8_BLOCK_M / F8_NWAVES;  // 32 query rows per wave
+constexpr int F8_D = 128;                          // d_qk = d_v
+constexpr int F8_SBLOCK = 128;                     // tokens per descale block
+constexpr int F8_TAU = 2;                          // re-base threshold, doublings
+constexpr float F8_PBIAS = 6.f;                    // p <= 2^(F8_TAU + F8_PBIAS) = 256
+
+static_assert(F8_SBLOCK % F8_BLOCK_N == 0 && F8_SBLOCK % F8_ROWS == 0 && F8_BLOCK_M % F8_SBLOCK == 0,
+              "tiles and wave rows must not straddle descale blocks");
+
+// e4m3 x e4m3 -> f32, 32x32 output, K = 64. Operand lane l: row/column l % 32,
+// bytes k = 32 (l / 32) + 0..31.
+__device__ inline f32x16_t mfma_f8(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline i32x8_t join8(u32x4_t lo, u32x4_t hi) {
+  return (i32x8_t){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Four e4m3 codes (RNE) in one dword, a in the lowest byte. Inputs are finite
+// and at most 256 in magnitude.
+__device__ inline unsigned pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (unsigned)w;
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(F8_NTHREADS, F8_NTHREADS),
+                          amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_kernel(const FwdParams p) {
+  constexpr int BLOCK_N = F8_BLOCK_N;
+  constexpr int NWAVES = F8_NWAVES;
+  constexpr int D = F8_D;
+  constexpr int K_STAGE = BLOCK_N * D;   // 64 key rows x 128 B
+  constexpr int VT_ROW = BLOCK_N;        // one dim row of the V^T tile: 64 keys
+  constexpr int V_STAGE = D * VT_ROW;    // 128 dim rows x 64 B
+  constexpr int NSTAGE = 3;
+  constexpr int LOADS_PER_TILE = 2;      // one 1 KB K load and one 1 KB V^T load per wave
+  static_assert(K_STAGE == 1024 * NWAVES && V_STAGE == 1024 * NWAVES, "one load per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (K_STAGE + V_STAGE)];
+  lds_u8* const k_lds = (lds_u8*)smem;
+  lds_u8* const v_lds = (lds_u8*)smem + NSTAGE * K_STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const bool group_b = wave >= NWAVES / 2;
+
+  const int BH = p.B * p.H;
+  int bh, qt;
+  map_block(blockIdx.x, p.n_qtiles, BH, CAUSAL, bh, qt);
+  const int q0 = qt * F8_BLOCK_M;
+  const int offset = p.Nkv - p.Nq;
+  const int nbq = (p.Nq + F8_SBLOCK - 1) / F8_SBLOCK;
+  const int nbk = (p.Nkv + F8_SBLOCK - 1) / F8_SBLOCK;
+
+  const uint8_t* __restrict__ qg = (const uint8_t*)p.q + (size_t)bh * p.Nq * D;
+  const uint8_t* __restrict__ kg = (const uint8_t*)p.k + (size_t)bh * p.Nkv * D;
+  const uint8_t* __restrict__ vg = (const uint8_t*)p.v + (size_t)bh * D * p.Nkv;
+  // Descales are read through the constant address space: the compiler may then use
+  // scalar loads inside the loop, which the tile loads' memory clobbers would
+  // otherwise forbid (a vector load there would wait for every tile load in flight).
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* const kds = (cfloat*)(p.k_descale + (size_t)bh * nbk);
+  cfloat* const vds = (cfloat*)(p.v_descale + (size_t)bh * nbk);
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) kv_end = min(p.Nkv, max(0, q0 + F8_BLOCK_M + offset));
+  const int ntiles = (kv_end + BLOCK_N - 1) / BLOCK_N;
+
+  // ---- Q^T fragments (B operand of S^T): query l32, dims 64 ks + 32 half + 0..31.
+  const int wq0 = q0 + wave * F8_ROWS;
+  const int my_q = wq0 + l32;
+  i32x8_t qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (my_q < p.Nq) {
+      const uint8_t* src = qg + (size_t)my_q * D + 64 * ks + 32 * half;
+      lo = *(const u32x4_t*)src;
+      hi = *(const u32x4_t*)(src + 16);
+    }
+    qf[ks] = join8(lo, hi);
+  }
+  // The wave's rows share one Q descale block (a wave past N_q reads the last one).
+  const float dq = ((cfloat*)p.q_descale)[(size_t)bh * nbq + min(wq0, p.Nq - 1) / F8_SBLOCK];
+  // dv_ref: the head's largest V descale.
+  float dv_ref = 0.f;
+  for (int i = lane; i < nbk; i += 64) dv_ref = fmaxf(dv_ref, vds[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) dv_ref = fmaxf(dv_ref, __shfl_xor(dv_ref, off));
+  const float c = p.scale_log2 * dq;
+  const float log2_dv_ref = dv_ref > 0.f ? __builtin_amdgcn_logf(dv_ref) : 0.f;
+
+  // ---- Direct-to-LDS tile loads; wave w fills bytes [1024 w, 1024 w + 1024) of a stage.
+  // K stage: 64 rows of 128 B, chunk c of row r at position c ^ ((r >> 1) & 7).
+  // V^T stage: 128 dim rows of 64 B, chunk c of row r at position c ^ ((r >> 2) & 3).
+  int k_off, v_off, v_key;
+  {
+    const int r = wave * 8 + lane / 8;
+    k_off = r * D + ((lane % 8) ^ ((r >> 1) & 7)) * 16;
+  }
+  {
+    const int r = wave * 16 + lane / 4;
+    const int cc = (lane % 4) ^ ((r >> 2) & 3);
+    v_key = cc * 16;  // first key of the lane's chunk within the tile
+    v_off = r * p.Nkv + v_key;
+  }
+  const unsigned v_bytes = (unsigned)(D * p.Nkv);
+  const i32x4_t v_rs = make_rsrc(vg, (int)v_bytes);
+  auto k_rsrc = [&](int j) {
+    const int key0 = min(j * BLOCK_N, p.Nkv);
+    return make_rsrc(kg + (size_t)key0 * D, (p.Nkv - key0) * D);
+  };
+  // V^T rows continue into the next dim row, so chunks past N_kv (N_kv is a multiple
+  // of 16) are pointed past the end of the resource, which reads them as zeros.
+  auto v_voff = [&](int j) {
+    const int key0 = j * BLOCK_N;
+    return (key0 + v_key < p.Nkv) ? v_off + key0 : (int)v_bytes;
+  };
+  auto issue_k = [&](int j, auto stage) {
+    buffer_load_lds16(k_rsrc(j), k_lds + int(stage) * K_STAGE + wave * 1024, k_off);
+  };
+  auto issue_v = [&](int j, auto stage) {
+    buffer_load_lds16(v_rs, v_lds + int(stage) * V_STAGE + wave * 1024, v_voff(j));
+  };
+
+  // ---- Per-lane LDS read offsets.
+  // K operand of S^T, key block kb, K-step ks: row 32 kb + l32, chunks 4 ks + 2 half + u.
+  int koff[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[ks][u] = l32 * D + ((4 * ks + 2 * half + u) ^ ((l32 >> 1) & 7)) * 16;
+  // V^T operand of O^T, dim block db: row 32 db + l32, chunks 2 half + u.
+  int voff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) voff[u] = l32 * VT_ROW + ((2 * half + u) ^ ((l32 >> 2) & 3)) * 16;
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  f32x16_t sacc[2];
+  i32x8_t pf;                // P^T B operand (e4m3) between softmax and PV
+  float m_ref = -INFINITY;   // running reference max, log2 units (bias excluded)
+  float l_part = 0.f;
+
+  auto s_phase = [&](auto stage) {
+    const lds_u8* st = k_lds + int(stage) * K_STAGE;
+    i32x8_t kf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kf[kb][ks] = join8(lds_read128(st + koff[ks][0] + kb * 32 * D),
+                           lds_read128(st + koff[ks][1] + kb * 32 * D));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_f8(kf[kb][ks], qf[ks], sacc[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto pv_phase = [&](auto stage, auto hook) {
+    const lds_u8* st = v_lds + int(stage) * V_STAGE;
+    i32x8_t vf[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      vf[db] = join8(lds_read128(st + voff[0] + db * 32 * VT_ROW),
+                     lds_read128(st + voff[1] + db * 32 * VT_ROW));
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      oacc[db] = mfma_f8(vf[db], pf, oacc[db]);
+      hook(db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no_hook = [](int) {};
+
+  auto softmax = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int blk = (j * BLOCK_N) / F8_SBLOCK;
+    const float ct = c * kds[blk];
+    const float dv = vds[blk];
+    // log2(dv / dv_ref) <= 0; a zero block (all codes 0) keeps the bias 0.
+    const float vbias = dv > 0.f ? __builtin_amdgcn_logf(dv) - log2_dv_ref : 0.f;
+    const float inv_ratio = __builtin_amdgcn_exp2f(-vbias);
+    int room = 0;
+    auto visible = [&](int kb, int r) { return kb * 32 + (r >> 2) * 8 + (r & 3) <= room; };
+    if constexpr (MASK) {
+      const int limit = CAUSAL ? min(p.Nkv - 1, my_q + offset) : p.Nkv - 1;
+      room = limit - j * BLOCK_N - half * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!visible(kb, r)) sacc[kb][r] = -INFINITY;
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_halves(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * ct;
+    const bool grow = mt > m_ref + (float)F8_TAU;
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
+      m_ref = grow ? mt : m_ref;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float nm = ((m_ref == -INFINITY) ? 0.f : -m_ref) + F8_PBIAS + vbias;
+    float psum = 0.f;
+    unsigned w[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], ct, nm));
+        if constexpr (MASK) e = visible(kb, r) ? e : 0.f;
+        pv[r] = e;
+        psum += e;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[kb][q] = pack4_fp8(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
+    }
+    // Lanes 0-31 keep key block 0 and receive the partner's block-0 dwords; lanes
+    // 32-63 keep block 1 and receive the partner's block-1 dwords.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const auto r = __builtin_amdgcn_permlane32_swap(w[0][q], w[1][q], false, false);
+      pf[2 * q] = (int)r[0];
+      pf[2 * q + 1] = (int)r[1];
+    }
+    l_part += psum * inv_ratio;
+  };
+
+  int j_plain = min(ntiles, p.Nkv / BLOCK_N);
+  if (CAUSAL) j_plain = min(j_plain, max(0, (q0 + offset + 1) / BLOCK_N));
+  const int wave_last_key = wq0 + F8_ROWS - 1 + offset;
+  auto active = [&](int j) { return !CAUSAL || j * BLOCK_N <= wave_last_key; };
+  constexpr std::false_type PLAIN{};
+  constexpr std::true_type MASKED{};
+
+  // Same barrier protocol as the 16-bit kernel: barrier j needs K(j) and V(j-1);
+  // K(j+2) and V(j+1) are issued after it.
+  auto pin_s = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(sacc[kb]));
+  };
+  auto pin_p = [&]() { asm volatile("" : "+v"(pf)); };
+  auto barrier_and_issue = [&](int j, auto k_next, auto v_next) {
+    tile_barrier<LOADS_PER_TILE>();
+    issue_k(j + 2, k_next);
+    issue_v(j + 1, v_next);
+  };
+  // The loads of an unrolled iteration go out between its PV products.
+  auto spread_issue = [&](int j, auto k_next, auto v_next) {
+    const i32x4_t krs = k_rsrc(j + 2);
+    lds_u8* kdst = k_lds + int(k_next) * K_STAGE + wave * 1024;
+    const int vo = v_voff(j + 1);
+    lds_u8* vdst = v_lds + int(v_next) * V_STAGE + wave * 1024;
+    return [=](int step) {
+      if (step == 0) buffer_load_lds16(krs, kdst, k_off);
+      if (step == 2) buffer_load_lds16(v_rs, vdst, vo);
+    };
+  };
+  auto plain_iter = [&](int j, auto r_tag) {
+    constexpr int R = decltype(r_tag)::value;
+    constexpr std::integral_constant<int, R> k_cur{};
+    constexpr std::integral_constant<int, (R + 2) % NSTAGE> v_prev{};
+    constexpr std::integral_constant<int, (R + 2) % NSTAGE> k_next{};
+    constexpr std::integral_constant<int, (R + 1) % NSTAGE> v_next{};
+    if (group_b) {
+      tile_barrier<LOADS_PER_TILE>();
+      pin_s();
+    }
+    softmax(j - 1, PLAIN);
+    if (!group_b) {
+      pin_p();
+      tile_barrier<LOADS_PER_TILE>();
+    }
+    pv_phase(v_prev, spread_issue(j, k_next, v_next));
+    s_phase(k_cur);
+  };
+  auto any_iter = [&](int j) {
+    const int r = j % NSTAGE;
+    if (group_b) {
+      barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+      pin_s();
+    }
+    if (active(j - 1)) {
+      if (j - 1 < j_plain) softmax(j - 1, PLAIN); else softmax(j - 1, MASKED);
+    }
+    if (!group_b) {
+      pin_p();
+      barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
+    }
+    if (active(j - 1)) pv_phase((r + 2) % NSTAGE, no_hook);
+    if (active(j)) s_phase(r);
+  };
+  if (ntiles > 0) {
+    issue_k(0, 0);
+    issue_k(1, 1);
+    issue_v(0, 0);
+    barrier_and_issue(0, 2, 1);
+    if (active(0)) s_phase(0);
+    const int j_last_plain = min(j_plain, ntiles - 1);
+    int j = 1;
+    for (; j + 2 <= j_last_plain; j += 3) {
+      plain_iter(j, std::integral_constant<int, 1>{});
+      plain_iter(j + 1, std::integral_constant<int, 2>{});
+      plain_iter(j + 2, std::integral_constant<int, 0>{});
+    }
+    for (; j < ntiles; ++j) any_iter(j);
+    if (group_b) tile_barrier<LOADS_PER_TILE>();
+    if (active(ntiles - 1)) {
+      if (ntiles - 1 < j_plain) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
+    }
+    if (!group_b) tile_barrier<LOADS_PER_TILE>();
+    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE, no_hook);
+  }
+
+  __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end
+
+  // ---- Epilogue: O = dv_ref * acc / l (bf16, RNE), LSE = ln2 * (m_ref - PBIAS + log2 l).
+  const float l = sum_halves(l_part);
+  const bool any = l > 0.f;
+  const float inv = any ? dv_ref * __builtin_amdgcn_rcpf(l) : 0.f;
+  if (my_q < p.Nq) {
+    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * D * 2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x2_t a = {oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv};
+        const f32x2_t b = {oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv};
+        u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
+                     __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
+        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
+      }
+    if (half == 0)
+      p.lse[(size_t)bh * p.Nq + my_q] =
+          any ? 0.69314718055994531f * (m_ref - F8_PBIAS + __builtin_amdgcn_logf(l)) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdParams& p0, bool causal, hipStream_t stream) {
+  FwdParams p = p0;
+  p.n_qtiles = (p.Nq + F8_BLOCK_M - 1) / F8_BLOCK_M;
+  const int grid = p.n_qtiles * p.B * p.H;
+  if (causal)
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3(grid), dim3(F8_NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, dim3(grid), dim3(F8_NTHREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace exattn

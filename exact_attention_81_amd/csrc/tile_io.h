@@ -1,0 +1,54 @@
+// Direct-to-LDS tile loads and partial-wait barriers shared by the gfx950
+// attention kernels.
+#pragma once
+
+#include "device.h"
+
+namespace exattn {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource word 3 for raw 32-bit-format buffers on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format.
+__device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return (i32x4_t){(int)(unsigned)a, (int)((a >> 32) & 0xffffu), bytes, kBufferFlags};
+}
+
+// 16 bytes per lane from `rsrc` at byte offset `voff` into LDS at dst + 16 * lane
+// (buffer_load_dwordx4 ... lds, LDS base in m0); offsets at or past the resource
+// size read as 0. Written as inline assembly so that the compiler does not track
+// these LDS writes: it would otherwise wait for every one of them (vmcnt(0))
+// before each ds_read_b64_tr_b16, which defeats loading tiles ahead. The waves
+// wait for them explicitly in tile_barrier. No other code in these kernels uses m0.
+__device__ inline void buffer_load_lds16(i32x4_t rsrc, lds_u8* dst, int voff) {
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding and
+// its LDS operations are done, then meet the other waves. Unlike __syncthreads
+// this leaves the newest N tile loads in flight.
+template <int N>
+__device__ inline void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ inline u32x4_t lds_read128(const lds_u8* p) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)p;
+}
+
+}  // namespace exattn

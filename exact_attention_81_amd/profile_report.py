@@ -30,6 +30,7 @@ from . import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_RE = re.compile(r"attn_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false)>")
+FP8_RE = re.compile(r"attn_fwd_fp8_kernel<(true|false)>")
 
 
 def _one(pattern_dir: str, suffix: str) -> str:
@@ -45,6 +46,11 @@ def short_name(name: str) -> str:
         dqk, dv, causal, tau, f16 = m.groups()
         return (f"attn_fwd_kernel d{dqk}x{dv} {'causal' if causal == 'true' else 'noncausal'} "
                 f"tau{tau} {'fp16' if f16 == 'true' else 'bf16'}")
+    m = FP8_RE.search(name)
+    if m:
+        return f"attn_fwd_fp8_kernel d128x128 {'causal' if m.group(1) == 'true' else 'noncausal'} e4m3"
+    if "quantize_kernel" in name:
+        return "quantize_kernel (e4m3 prep)"
     if "neg" in name:
         return "copy (torch.neg, float32)"
     return name[:60]
@@ -71,22 +77,29 @@ def counter_per_dispatch(d: str, counter: str):
 
 
 def algorithmic_bytes(w) -> int:
-    """Q, K, V read once, O and LSE written once."""
+    """Q, K, V read once, O and LSE written once (fp8: 1-byte inputs plus descales)."""
     bh = w.B * w.H
-    return 2 * bh * (w.N_q * w.d_qk + w.N_kv * w.d_qk + w.N_kv * w.d_v + w.N_q * w.d_v) + 4 * bh * w.N_q
+    ins = w.N_q * w.d_qk + w.N_kv * w.d_qk + w.N_kv * w.d_v
+    if w.fp8:
+        nb = lambda n: (n + 127) // 128
+        return bh * (ins + 4 * (nb(w.N_q) + 2 * nb(w.N_kv)) + 2 * w.N_q * w.d_v + 4 * w.N_q)
+    return bh * (2 * ins + 2 * w.N_q * w.d_v + 4 * w.N_q)
 
 
 def workloads_of(name: str):
     if name.startswith("sweep"):
         n = int(name[5:])
         return [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
-    if name in ("tiny", "asym"):
+    if name in ("tiny", "asym", "fp8"):
         return [synth.workload(name)]
     return [synth.workload("single", causal=c) for c in (False, True)]
 
 
 def variant_key(w) -> str:
-    return (f"attn_fwd_kernel d{w.d_qk}x{w.d_v} {'causal' if w.causal else 'noncausal'} tau8 bf16")
+    mask = "causal" if w.causal else "noncausal"
+    if w.fp8:
+        return f"attn_fwd_fp8_kernel d128x128 {mask} e4m3"
+    return f"attn_fwd_kernel d{w.d_qk}x{w.d_v} {mask} tau8 bf16"
 
 
 def main():

@@ -7,6 +7,7 @@ generators.
 """
 from .attention import attention, attention_parallel, attention_rows, head, to_f64  # noqa: F401
 from .fp8 import (  # noqa: F401
+    BLOCK_TOKENS,
     E4M3_MAX,
     dequantize_blocks,
     e4m3_decode,
