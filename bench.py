@@ -99,6 +99,8 @@ def main():
                              "sweep2048", "sweep4096", "sweep8192", "sweep16384"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cold-runs", type=int, default=5,
+                    help="launches per variant timed after evicting the caches (0: none)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run a plain float32 copy of this many MiB "
                          "three times (calibrates the HBM byte counters of a profiler run)")
@@ -182,6 +184,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    # Cold caches: after the timed region, each launch is timed once more right after a
+    # 512 MiB fill that evicts L2 and the infinity cache (MALL).
+    cold = [[] for _ in inputs]
+    if args.cold_runs > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_runs):
+            for i, (w, launch) in enumerate(inputs):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                launch()
+                e1.record()
+                torch.cuda.synchronize()
+                cold[i].append(e0.elapsed_time(e1))
+        del flush
+
     prep_us = None
     if prep is not None:
         for _ in range(3):
@@ -212,9 +230,16 @@ def main():
     for i, (w, *_rest) in enumerate(inputs):
         durs = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
         avg_ms = sum(durs) / len(durs)
-        per.append({"variant": w.label(), "avg_launch_us": avg_ms * 1e3,
-                    "tflops": w.flops() / (avg_ms * 1e-3) / 1e12,
-                    "min_launch_us": min(durs) * 1e3})
+        srt = sorted(durs)
+        med_ms = 0.5 * (srt[(len(srt) - 1) // 2] + srt[len(srt) // 2])
+        rec = {"variant": w.label(), "avg_launch_us": avg_ms * 1e3,
+               "tflops": w.flops() / (avg_ms * 1e-3) / 1e12,
+               "median_launch_us": med_ms * 1e3, "min_launch_us": srt[0] * 1e3}
+        if cold[i]:
+            cavg = sum(cold[i]) / len(cold[i])
+            rec["cold_avg_launch_us"] = cavg * 1e3
+            rec["cold_tflops"] = w.flops() / (cavg * 1e-3) / 1e12
+        per.append(rec)
     dt = "fp8" if fp8 else "bf16"
     peak = PEAK[dt]
     for p in per:

@@ -10,12 +10,12 @@
 // Evolution", FlashAttention-3's FP8 path).
 //
 // The schedule is the one of the 16-bit kernel: 8 waves of 32 query rows,
-// 64-key tiles streamed into 3-stage LDS rings by direct-to-LDS loads, one
+// key tiles streamed into 3-stage LDS rings by direct-to-LDS loads, one
 // barrier per tile, and two wave groups half an iteration apart so that one
 // wave of every SIMD computes exponentials while the other feeds the matrix
 // core.
 //
-// Scales. A 64-key tile lies inside one 128-key descale block and a wave's 32
+// Scales. A 128-key tile is one descale block of K and V and a wave's 32
 // query rows inside one 128-query block, so the score of a tile is
 //     s * log2(e) = (scale * log2(e) * dq * dk) * (codes_q . codes_k),
 // one scalar per wave and tile times the MFMA result. P is taken as
@@ -44,7 +44,7 @@ namespace exattn {
 namespace {
 
 constexpr int F8_BLOCK_M = 256;
-constexpr int F8_BLOCK_N = 64;
+constexpr int F8_BLOCK_N = 128;
 constexpr int F8_NWAVES = 8;
 constexpr int F8_NTHREADS = 64 * F8_NWAVES;
 constexpr int F8_ROWS = F8_BLOCK_M / F8_NWAVES;  // 32 query rows per wave
@@ -82,12 +82,16 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   constexpr int BLOCK_N = F8_BLOCK_N;
   constexpr int NWAVES = F8_NWAVES;
   constexpr int D = F8_D;
-  constexpr int K_STAGE = BLOCK_N * D;   // 64 key rows x 128 B
-  constexpr int VT_ROW = BLOCK_N;        // one dim row of the V^T tile: 64 keys
-  constexpr int V_STAGE = D * VT_ROW;    // 128 dim rows x 64 B
+  constexpr int K_STAGE = BLOCK_N * D;   // 128 key rows x 128 B
+  constexpr int VT_ROW = BLOCK_N;        // one dim row of the V^T tile: 128 keys
+  constexpr int V_STAGE = D * VT_ROW;    // 128 dim rows x 128 B
   constexpr int NSTAGE = 3;
-  constexpr int LOADS_PER_TILE = 2;      // one 1 KB K load and one 1 KB V^T load per wave
-  static_assert(K_STAGE == 1024 * NWAVES && V_STAGE == 1024 * NWAVES, "one load per wave");
+  constexpr int NKB = BLOCK_N / 32;      // 32-key blocks of S^T
+  constexpr int NKC = BLOCK_N / 64;      // 64-key steps of the PV product
+  constexpr int K_PER = K_STAGE / 1024 / NWAVES;  // 1 KB loads per wave and tile
+  constexpr int V_PER = V_STAGE / 1024 / NWAVES;
+  constexpr int LOADS_PER_TILE = K_PER + V_PER;
+  static_assert(K_STAGE % (1024 * NWAVES) == 0 && V_STAGE % (1024 * NWAVES) == 0, "even loads");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * (K_STAGE + V_STAGE)];
   lds_u8* const k_lds = (lds_u8*)smem;
@@ -147,18 +151,21 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   const float log2_dv_ref = dv_ref > 0.f ? __builtin_amdgcn_logf(dv_ref) : 0.f;
 
   // ---- Direct-to-LDS tile loads; wave w fills bytes [1024 w, 1024 w + 1024) of a stage.
-  // K stage: 64 rows of 128 B, chunk c of row r at position c ^ ((r >> 1) & 7).
-  // V^T stage: 128 dim rows of 64 B, chunk c of row r at position c ^ ((r >> 2) & 3).
-  int k_off, v_off, v_key;
-  {
-    const int r = wave * 8 + lane / 8;
-    k_off = r * D + ((lane % 8) ^ ((r >> 1) & 7)) * 16;
+  // Both stages hold rows of 128 B (K: 128 key rows; V^T: 128 dim rows of 128 keys),
+  // chunk c of row r at position c ^ ((r >> 1) & 7). Load t of wave w fills rows
+  // 8 (w + 8 t) .. 8 (w + 8 t) + 7.
+  int k_off[K_PER], v_off[V_PER], v_key[V_PER];
+#pragma unroll
+  for (int t = 0; t < K_PER; ++t) {
+    const int r = (wave + t * NWAVES) * 8 + lane / 8;
+    k_off[t] = r * D + ((lane % 8) ^ ((r >> 1) & 7)) * 16;
   }
-  {
-    const int r = wave * 16 + lane / 4;
-    const int cc = (lane % 4) ^ ((r >> 2) & 3);
-    v_key = cc * 16;  // first key of the lane's chunk within the tile
-    v_off = r * p.Nkv + v_key;
+#pragma unroll
+  for (int t = 0; t < V_PER; ++t) {
+    const int r = (wave + t * NWAVES) * 8 + lane / 8;
+    const int cc = (lane % 8) ^ ((r >> 1) & 7);
+    v_key[t] = cc * 16;  // first key of the lane's chunk within the tile
+    v_off[t] = r * p.Nkv + v_key[t];
   }
   const unsigned v_bytes = (unsigned)(D * p.Nkv);
   const i32x4_t v_rs = make_rsrc(vg, (int)v_bytes);
@@ -168,15 +175,20 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   };
   // V^T rows continue into the next dim row, so chunks past N_kv (N_kv is a multiple
   // of 16) are pointed past the end of the resource, which reads them as zeros.
-  auto v_voff = [&](int j) {
+  auto v_voff = [&](int j, int t) {
     const int key0 = j * BLOCK_N;
-    return (key0 + v_key < p.Nkv) ? v_off + key0 : (int)v_bytes;
+    return (key0 + v_key[t] < p.Nkv) ? v_off[t] + key0 : (int)v_bytes;
   };
   auto issue_k = [&](int j, auto stage) {
-    buffer_load_lds16(k_rsrc(j), k_lds + int(stage) * K_STAGE + wave * 1024, k_off);
+    const i32x4_t rs = k_rsrc(j);
+#pragma unroll
+    for (int t = 0; t < K_PER; ++t)
+      buffer_load_lds16(rs, k_lds + int(stage) * K_STAGE + (wave + t * NWAVES) * 1024, k_off[t]);
   };
   auto issue_v = [&](int j, auto stage) {
-    buffer_load_lds16(v_rs, v_lds + int(stage) * V_STAGE + wave * 1024, v_voff(j));
+#pragma unroll
+    for (int t = 0; t < V_PER; ++t)
+      buffer_load_lds16(v_rs, v_lds + int(stage) * V_STAGE + (wave + t * NWAVES) * 1024, v_voff(j, t));
   };
 
   // ---- Per-lane LDS read offsets.
@@ -186,54 +198,61 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int u = 0; u < 2; ++u) koff[ks][u] = l32 * D + ((4 * ks + 2 * half + u) ^ ((l32 >> 1) & 7)) * 16;
-  // V^T operand of O^T, dim block db: row 32 db + l32, chunks 2 half + u.
-  int voff[2];
+  // V^T operand of O^T, dim block db, key step kc: row 32 db + l32, chunks
+  // 4 kc + 2 half + u.
+  int voff[NKC][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) voff[u] = l32 * VT_ROW + ((2 * half + u) ^ ((l32 >> 2) & 3)) * 16;
+  for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) voff[kc][u] = l32 * VT_ROW + ((4 * kc + 2 * half + u) ^ ((l32 >> 1) & 7)) * 16;
 
   f32x16_t oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  f32x16_t sacc[2];
-  i32x8_t pf;                // P^T B operand (e4m3) between softmax and PV
+  f32x16_t sacc[NKB];
+  i32x8_t pf[NKC];           // P^T B operands (e4m3) between softmax and PV
   float m_ref = -INFINITY;   // running reference max, log2 units (bias excluded)
   float l_part = 0.f;
 
+  // S(j): S^T = K_j Q^T. Operands are read two products ahead of their MFMA.
   auto s_phase = [&](auto stage) {
     const lds_u8* st = k_lds + int(stage) * K_STAGE;
-    i32x8_t kf[2][2];
+    constexpr int STEPS = 2 * NKB;  // step = ks * NKB + kb
+    auto kread = [&](int step) {
+      const int ks = step / NKB, kb = step % NKB;
+      return join8(lds_read128(st + koff[ks][0] + kb * 32 * D), lds_read128(st + koff[ks][1] + kb * 32 * D));
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        kf[kb][ks] = join8(lds_read128(st + koff[ks][0] + kb * 32 * D),
-                           lds_read128(st + koff[ks][1] + kb * 32 * D));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    }
+    i32x8_t kf[2] = {kread(0), kread(1)};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma_f8(kf[kb][ks], qf[ks], sacc[kb]);
+    for (int step = 0; step < STEPS; ++step) {
+      const i32x8_t cur = kf[step % 2];
+      if (step + 2 < STEPS) kf[step % 2] = kread(step + 2);
+      sacc[step % NKB] = mfma_f8(cur, qf[step / NKB], sacc[step % NKB]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // PV(j): O^T += V_j^T P_j^T, operands two products ahead; hook(step) issues tile loads.
   auto pv_phase = [&](auto stage, auto hook) {
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
-    i32x8_t vf[4];
+    constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
+    auto vread = [&](int step) {
+      const int kc = step / 4, db = step % 4;
+      return join8(lds_read128(st + voff[kc][0] + db * 32 * VT_ROW), lds_read128(st + voff[kc][1] + db * 32 * VT_ROW));
+    };
+    i32x8_t vf[2] = {vread(0), vread(1)};
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      vf[db] = join8(lds_read128(st + voff[0] + db * 32 * VT_ROW),
-                     lds_read128(st + voff[1] + db * 32 * VT_ROW));
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      oacc[db] = mfma_f8(vf[db], pf, oacc[db]);
-      hook(db);
+    for (int step = 0; step < STEPS; ++step) {
+      const i32x8_t cur = vf[step % 2];
+      if (step + 2 < STEPS) vf[step % 2] = vread(step + 2);
+      oacc[step % 4] = mfma_f8(cur, pf[step / 4], oacc[step % 4]);
+      hook(step);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -242,7 +261,9 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int blk = (j * BLOCK_N) / F8_SBLOCK;
-    const float ct = c * kds[blk];
+    // Kept positive (a zero descale or scale gives 1e-30, which moves no score by a
+    // representable amount) so that a masked score of -inf gives p = 0 by itself.
+    const float ct = fmaxf(c * kds[blk], 1e-30f);
     const float dv = vds[blk];
     // log2(dv / dv_ref) <= 0; a zero block (all codes 0) keeps the bias 0.
     const float vbias = dv > 0.f ? __builtin_amdgcn_logf(dv) - log2_dv_ref : 0.f;
@@ -253,14 +274,14 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
       const int limit = CAUSAL ? min(p.Nkv - 1, my_q + offset) : p.Nkv - 1;
       room = limit - j * BLOCK_N - half * 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (!visible(kb, r)) sacc[kb][r] = -INFINITY;
     }
     float mx = sacc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = max_halves(mx);
@@ -277,28 +298,29 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     }
     const float nm = ((m_ref == -INFINITY) ? 0.f : -m_ref) + F8_PBIAS + vbias;
     float psum = 0.f;
-    unsigned w[2][4];
+    unsigned w[NKB][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], ct, nm));
-        if constexpr (MASK) e = visible(kb, r) ? e : 0.f;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], ct, nm));
         pv[r] = e;
         psum += e;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[kb][q] = pack4_fp8(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
     }
-    // Lanes 0-31 keep key block 0 and receive the partner's block-0 dwords; lanes
-    // 32-63 keep block 1 and receive the partner's block-1 dwords.
+    // For each 64 keys (blocks 2 kc, 2 kc + 1): lanes 0-31 keep block 2 kc and receive
+    // the partner's dwords of it; lanes 32-63 keep block 2 kc + 1 likewise.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const auto r = __builtin_amdgcn_permlane32_swap(w[0][q], w[1][q], false, false);
-      pf[2 * q] = (int)r[0];
-      pf[2 * q + 1] = (int)r[1];
-    }
+    for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto r = __builtin_amdgcn_permlane32_swap(w[2 * kc][q], w[2 * kc + 1][q], false, false);
+        pf[kc][2 * q] = (int)r[0];
+        pf[kc][2 * q + 1] = (int)r[1];
+      }
     l_part += psum * inv_ratio;
   };
 
@@ -313,23 +335,32 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   // K(j+2) and V(j+1) are issued after it.
   auto pin_s = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(sacc[kb]));
+    for (int kb = 0; kb < NKB; ++kb) asm volatile("" : "+v"(sacc[kb]));
   };
-  auto pin_p = [&]() { asm volatile("" : "+v"(pf)); };
+  auto pin_p = [&]() {
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) asm volatile("" : "+v"(pf[kc]));
+  };
   auto barrier_and_issue = [&](int j, auto k_next, auto v_next) {
     tile_barrier<LOADS_PER_TILE>();
     issue_k(j + 2, k_next);
     issue_v(j + 1, v_next);
   };
   // The loads of an unrolled iteration go out between its PV products.
+  constexpr int ISSUE_GAP = 4 * NKC / LOADS_PER_TILE;
+  static_assert(ISSUE_GAP >= 1, "one load per PV product at most");
   auto spread_issue = [&](int j, auto k_next, auto v_next) {
     const i32x4_t krs = k_rsrc(j + 2);
     lds_u8* kdst = k_lds + int(k_next) * K_STAGE + wave * 1024;
-    const int vo = v_voff(j + 1);
     lds_u8* vdst = v_lds + int(v_next) * V_STAGE + wave * 1024;
+    int vo[V_PER];
+#pragma unroll
+    for (int t = 0; t < V_PER; ++t) vo[t] = v_voff(j + 1, t);
     return [=](int step) {
-      if (step == 0) buffer_load_lds16(krs, kdst, k_off);
-      if (step == 2) buffer_load_lds16(v_rs, vdst, vo);
+      if (step % ISSUE_GAP != 0) return;
+      const int li = step / ISSUE_GAP;
+      if (li < K_PER) buffer_load_lds16(krs, kdst + li * NWAVES * 1024, k_off[li]);
+      else if (li < LOADS_PER_TILE) buffer_load_lds16(v_rs, vdst + (li - K_PER) * NWAVES * 1024, vo[li - K_PER]);
     };
   };
   auto plain_iter = [&](int j, auto r_tag) {
