@@ -216,7 +216,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   float m_ref = -INFINITY;   // running reference max, log2 units (bias excluded)
   float l_part = 0.f;
 
-  // S(j): S^T = K_j Q^T. Operands are read two products ahead of their MFMA.
+  // S(j): S^T = K_j Q^T. Operands are read one product ahead of their MFMA.
   auto s_phase = [&](auto stage) {
     const lds_u8* st = k_lds + int(stage) * K_STAGE;
     constexpr int STEPS = 2 * NKB;  // step = ks * NKB + kb
@@ -228,17 +228,17 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    i32x8_t kf[2] = {kread(0), kread(1)};
+    i32x8_t kf = kread(0);
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
-      const i32x8_t cur = kf[step % 2];
-      if (step + 2 < STEPS) kf[step % 2] = kread(step + 2);
+      const i32x8_t cur = kf;
+      if (step + 1 < STEPS) kf = kread(step + 1);
       sacc[step % NKB] = mfma_f8(cur, qf[step / NKB], sacc[step % NKB]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // PV(j): O^T += V_j^T P_j^T, operands two products ahead; hook(step) issues tile loads.
+  // PV(j): O^T += V_j^T P_j^T, operands one product ahead; hook(step) issues tile loads.
   auto pv_phase = [&](auto stage, auto hook) {
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
     constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
@@ -246,11 +246,11 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
       const int kc = step / 4, db = step % 4;
       return join8(lds_read128(st + voff[kc][0] + db * 32 * VT_ROW), lds_read128(st + voff[kc][1] + db * 32 * VT_ROW));
     };
-    i32x8_t vf[2] = {vread(0), vread(1)};
+    i32x8_t vf = vread(0);
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
-      const i32x8_t cur = vf[step % 2];
-      if (step + 2 < STEPS) vf[step % 2] = vread(step + 2);
+      const i32x8_t cur = vf;
+      if (step + 1 < STEPS) vf = vread(step + 1);
       oacc[step % 4] = mfma_f8(cur, pf[step / 4], oacc[step % 4]);
       hook(step);
       __builtin_amdgcn_sched_barrier(0);
