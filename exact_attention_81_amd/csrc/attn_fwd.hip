@@ -373,6 +373,10 @@ void attn_fwd_kernel(const FwdParams p) {
   if (CAUSAL) j_plain = min(j_plain, max(0, (q0 + offset + 1) / BLOCK_N));
   const int wave_last_key = wq0 + ROWS_PER_WAVE - 1 + offset;
   auto active = [&](int j) { return !CAUSAL || j * BLOCK_N <= wave_last_key; };
+  // Tile j needs no mask for this wave: its keys exist and every row of the wave sees them.
+  auto wave_plain = [&](int j) {
+    return j < j_plain || (j + 1) * BLOCK_N <= (CAUSAL ? min(p.Nkv, wq0 + offset + 1) : p.Nkv);
+  };
   constexpr std::false_type PLAIN{};
   constexpr std::true_type MASKED{};
 
@@ -455,7 +459,7 @@ void attn_fwd_kernel(const FwdParams p) {
       pin_s();
     }
     if (active(j - 1)) {
-      if (j - 1 < j_plain) softmax(j - 1, PLAIN); else softmax(j - 1, MASKED);
+      if (wave_plain(j - 1)) softmax(j - 1, PLAIN); else softmax(j - 1, MASKED);
     }
     if (!group_b) {
       pin_p();
@@ -481,7 +485,7 @@ void attn_fwd_kernel(const FwdParams p) {
     for (; j < ntiles; ++j) any_iter(j);
     if (group_b) tile_barrier<LOADS_PER_TILE>();
     if (active(ntiles - 1)) {
-      if (ntiles - 1 < j_plain) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
+      if (wave_plain(ntiles - 1)) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
     }
     if (!group_b) tile_barrier<LOADS_PER_TILE>();
     if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE, no_hook);

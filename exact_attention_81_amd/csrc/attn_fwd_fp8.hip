@@ -238,7 +238,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     }
   };
 
-  // PV(j): O^T += V_j^T P_j^T, operands one product ahead; hook(step) issues tile loads.
+  // PV(j): O^T += V_j^T P_j^T, operands two products ahead; hook(step) issues tile loads.
   auto pv_phase = [&](auto stage, auto hook) {
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
     constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
@@ -246,11 +246,11 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
       const int kc = step / 4, db = step % 4;
       return join8(lds_read128(st + voff[kc][0] + db * 32 * VT_ROW), lds_read128(st + voff[kc][1] + db * 32 * VT_ROW));
     };
-    i32x8_t vf = vread(0);
+    i32x8_t vf[2] = {vread(0), vread(1)};
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
-      const i32x8_t cur = vf;
-      if (step + 1 < STEPS) vf = vread(step + 1);
+      const i32x8_t cur = vf[step % 2];
+      if (step + 2 < STEPS) vf[step % 2] = vread(step + 2);
       oacc[step % 4] = mfma_f8(cur, pf[step / 4], oacc[step % 4]);
       hook(step);
       __builtin_amdgcn_sched_barrier(0);
