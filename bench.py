@@ -35,7 +35,7 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
                   for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "device.h", "tile_io.h",
-                            "launch.h")]
+                            "fp8_ops.h", "launch.h")]
 
 
 def kernel_source_hash() -> str:
