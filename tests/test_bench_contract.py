@@ -1,0 +1,40 @@
+"""bench.py's command-line contract and its JSON line (the GPU case runs a short bench)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("workload", ["tiny", "fp8"])
+def test_bench_line(workload):
+    print(f"[gpu-case] bench.py --workload {workload}", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
+                        "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--cold-runs", "1"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 3 and line["warmup"] == 1
+    assert line["value"] > 0 and line["ms_per_step"] > 0
+    roof = line["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+    assert roof["peak"] == (5000.0 if workload == "fp8" else 2500.0)
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert "workload" in line["config"]
+    for p in line["per_variant"]:
+        assert p["min_launch_us"] <= p["median_launch_us"] and p["cold_avg_launch_us"] > 0

@@ -1,0 +1,77 @@
+"""profile_report: parsing of rocprofv3 CSV output and the copy calibration."""
+import csv
+import json
+import os
+
+from exact_attention_81_amd import profile_report, synth
+
+KNAME = "void exattn::(anonymous namespace)::attn_fwd_kernel<128, 128, {c}, 8, false>(exattn::FwdParams)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>(...)"
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_short_names():
+    assert profile_report.short_name(KNAME.format(c="true")) == \
+        "attn_fwd_kernel d128x128 causal tau8 bf16"
+    assert profile_report.short_name(
+        "void exattn::(anonymous namespace)::attn_fwd_fp8_kernel<false>(exattn::FwdParams)") == \
+        "attn_fwd_fp8_kernel d128x128 noncausal e4m3"
+    assert profile_report.short_name(COPY) == "copy (torch.neg, float32)"
+
+
+def test_algorithmic_bytes():
+    w = synth.workload("single", causal=False)
+    assert profile_report.algorithmic_bytes(w) == 4 * 16 * (2048 * 128 * 2 * 4 + 2048 * 4)
+    f = synth.workload("fp8")
+    bh = 4 * 16
+    assert profile_report.algorithmic_bytes(f) == bh * (4096 * 128 * 3 + 4 * 3 * 32 + 2 * 4096 * 128 + 4 * 4096)
+
+
+def test_report_end_to_end(tmp_path):
+    d = str(tmp_path)
+    _write(f"{d}/stats/run_kernel_stats.csv",
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+           [[KNAME.format(c="false"), 10, 1.3e6, 1.3e5, 60.0, 1.25e5, 1.4e5, 1.0],
+            [KNAME.format(c="true"), 10, 0.85e6, 0.85e5, 40.0, 0.8e5, 0.9e5, 1.0]])
+    head = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    mib = 1024
+    # the copy reads and writes 1 GiB; FETCH_SIZE shows half of it (as on the box)
+    _write(f"{d}/fetch/run_counter_collection.csv", head,
+           [[COPY, "FETCH_SIZE", mib * 1024 / 2], [KNAME.format(c="false"), "FETCH_SIZE", 49000.0],
+            [KNAME.format(c="false"), "FETCH_SIZE", 50000.0], [KNAME.format(c="true"), "FETCH_SIZE", 74000.0]])
+    _write(f"{d}/write/run_counter_collection.csv", head,
+           [[COPY, "WRITE_SIZE", mib * 1024], [KNAME.format(c="false"), "WRITE_SIZE", 33280.0],
+            [KNAME.format(c="true"), "WRITE_SIZE", 33280.0]])
+    w0 = synth.workload("single", causal=False)
+    w1 = synth.workload("single", causal=True)
+    bench = {"kernel_source_sha": "abc", "roofline": {"kernel": f"attn_fwd_kernel ({w0.label()})"},
+             "per_variant": [{"variant": w0.label(), "avg_launch_us": 131.0, "tflops": 1000.0},
+                             {"variant": w1.label(), "avg_launch_us": 86.0, "tflops": 800.0}]}
+    with open(f"{d}/bench.json", "w") as fh:
+        fh.write("noise\n" + json.dumps(bench) + "\n")
+    with open(f"{d}/commands.txt", "w") as fh:
+        fh.write("python3 bench.py\n")
+    out = f"{d}/profiles"
+    import sys
+    argv = sys.argv
+    sys.argv = ["profile_report", "--workload", "single", "--bench-json", f"{d}/bench.json",
+                "--stats", f"{d}/stats", "--fetch", f"{d}/fetch", "--write", f"{d}/write",
+                "--copy-mib", str(mib), "--commands", f"{d}/commands.txt", "--out", out]
+    try:
+        profile_report.main()
+    finally:
+        sys.argv = argv
+    rec = json.load(open(f"{out}/attn_fwd_single_traffic.json"))
+    assert rec["copy_factor_fetch"] == 2.0 and rec["copy_factor_write"] == 1.0
+    assert rec["kernel_source_sha"] == "abc"
+    assert rec["dominant_variant"] == w0.label()
+    assert rec["hbm_bytes_per_launch"] == 49500.0 * 1024 * 2 + 33280.0 * 1024
+    text = open(f"{out}/attn_fwd_single.md").read()
+    assert "python3 bench.py" in text and "| 10 |" in text
