@@ -472,7 +472,14 @@ void attn_fwd_kernel(const FwdParams p) {
     issue_k(0, 0);
     issue_k(1, 1);
     issue_v(0, 0);
-    barrier_and_issue(0, 2, 1);
+    tile_barrier<LOADS_PER_TILE>();
+    // The compiler waits for the Q fragments at their first use, and since it does not
+    // see the tile loads it waits for every load (vmcnt(0)). Touching the fragments
+    // here, before K(2) and V(1) are issued, keeps that wait from covering those two.
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qf[s]));
+    issue_k(2, 2);
+    issue_v(1, 1);
     if (active(0)) s_phase(0);
     // Iterations j <= j_plain have a plain softmax and every wave active.
     const int j_last_plain = min(j_plain, ntiles - 1);

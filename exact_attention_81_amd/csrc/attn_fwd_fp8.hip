@@ -111,26 +111,23 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   // ---- Q^T fragments (B operand of S^T): query l32, dims 64 ks + 32 half + 0..31.
   const int wq0 = q0 + wave * F8_ROWS;
   const int my_q = wq0 + l32;
+  // Rows past N_q repeat row N_q - 1: their results are never stored, and loading
+  // unconditionally keeps the compiler from waiting for these loads (to merge them
+  // with zeros) before the first tile loads are issued.
   i32x8_t qf[2];
+  {
+    const uint8_t* src = qg + (size_t)min(my_q, p.Nq - 1) * D + 32 * half;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (my_q < p.Nq) {
-      const uint8_t* src = qg + (size_t)my_q * D + 64 * ks + 32 * half;
-      lo = *(const u32x4_t*)src;
-      hi = *(const u32x4_t*)(src + 16);
-    }
-    qf[ks] = join8(lo, hi);
+    for (int ks = 0; ks < 2; ++ks)
+      qf[ks] = join8(*(const u32x4_t*)(src + 64 * ks), *(const u32x4_t*)(src + 64 * ks + 16));
   }
   // The wave's rows share one Q descale block (a wave past N_q reads the last one).
   const float dq = ((cfloat*)p.q_descale)[(size_t)bh * nbq + min(wq0, p.Nq - 1) / F8_SBLOCK];
-  // dv_ref: the head's largest V descale.
-  float dv_ref = 0.f;
-  for (int i = lane; i < nbk; i += 64) dv_ref = fmaxf(dv_ref, vds[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) dv_ref = fmaxf(dv_ref, __shfl_xor(dv_ref, off));
+  // dv_ref: the head's largest V descale. The first 64 descales are loaded here and
+  // reduced after the first tile barrier (see the prologue below).
+  float dv_ref = lane < nbk ? vds[lane] : 0.f;
+  float log2_dv_ref = 0.f;
   const float c = p.scale_log2 * dq;
-  const float log2_dv_ref = dv_ref > 0.f ? __builtin_amdgcn_logf(dv_ref) : 0.f;
 
   // ---- Direct-to-LDS tile loads; wave w fills bytes [1024 w, 1024 w + 1024) of a stage.
   // Both stages hold rows of 128 B (K: 128 key rows; V^T: 128 dim rows of 128 keys),
@@ -383,7 +380,19 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     issue_k(0, 0);
     issue_k(1, 1);
     issue_v(0, 0);
-    barrier_and_issue(0, 2, 1);
+    tile_barrier<LOADS_PER_TILE>();
+    // The compiler waits for its own loads (the Q fragments, the V descales) at their
+    // first use, and since it does not see the tile loads it waits for every load
+    // (vmcnt(0)). Using them here, before K(2) and V(1) are issued, keeps that wait
+    // from covering those two.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(qf[ks]));
+    for (int i = lane + 64; i < nbk; i += 64) dv_ref = fmaxf(dv_ref, vds[i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dv_ref = fmaxf(dv_ref, __shfl_xor(dv_ref, off));
+    log2_dv_ref = dv_ref > 0.f ? __builtin_amdgcn_logf(dv_ref) : 0.f;
+    issue_k(2, 2);
+    issue_v(1, 1);
     if (active(0)) s_phase(0);
     const int j_last_plain = min(j_plain, ntiles - 1);
     int j = 1;
