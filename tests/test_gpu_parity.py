@@ -95,6 +95,34 @@ def test_ragged(nq, nkv, causal, dims):
     check_full(2, 3, nq, nkv, dims[0], dims[1], causal, seed=nq * 7 + nkv + dims[0])
 
 
+# ------------------------------------------------------------------ many work items
+# More (query tile, head) items than the GPU's 256 compute units, in shapes whose
+# sequence lengths are whole query tiles: several workgroups run on each compute unit
+# in turn, heavy and light causal tiles mixed.
+MANY_ITEM_CASES = [
+    (3, 88, 256, 256, 128, 128, False),     # 264 items: 8 workgroups take a second one
+    (3, 88, 256, 256, 128, 128, True),
+    (2, 96, 512, 512, 128, 128, True),      # 384 items, heavy/light causal pairs
+    (4, 72, 256, 768, 128, 128, True),      # N_q < N_kv: bottom-right causal alignment
+    (4, 72, 256, 768, 64, 64, False),
+    (2, 96, 512, 1024, 192, 128, True),
+    (4, 64, 512, 512, 64, 64, True),        # 512 items, two rounds
+    (2, 64, 1024, 1024, 128, 128, False),   # 512 items
+    (1, 128, 1024, 1024, 128, 128, True),   # 512 items, four query tiles per head
+]
+
+
+@pytest.mark.parametrize("case", MANY_ITEM_CASES, ids=lambda c: "B{}H{}_{}x{}_d{}x{}_{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "noncausal"))
+def test_many_items(case):
+    B, H, nq, nkv, dqk, dv, causal = case
+    check_full(B, H, nq, nkv, dqk, dv, causal, seed=B * 1000 + H + nq + nkv + dqk)
+
+
+def test_many_items_fp16():
+    check_full(3, 88, 256, 512, 128, 128, True, seed=91, dtype=torch.float16)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp16(causal):
     check_full(2, 4, 333, 517, 128, 128, causal, seed=11, dtype=torch.float16)
