@@ -16,3 +16,4 @@ from .fp8 import (  # noqa: F401
     quantize_blocks,
     rotation,
 )
+from .decode import attention_gqa, head_keys, kv_head, merge  # noqa: F401
