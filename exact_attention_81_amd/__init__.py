@@ -8,7 +8,9 @@ the library has not been built.
 """
 from .binding import (  # noqa: F401
     AttnError,
+    attn_decode_splits,
     attn_fwd,
+    attn_fwd_decode,
     attn_fwd_fp8,
     attn_fwd_tau,
     attn_quantize_fp8,

@@ -54,6 +54,13 @@ def load_library() -> ctypes.CDLL:
     lib.attn_quantize_fp8.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp,
+                                    ctypes.c_size_t, vp]
+    lib.attn_fwd_decode.restype = i
+    lib.attn_decode_splits.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_decode_splits.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -176,4 +183,53 @@ def attn_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, *, causal: bool =
                                      _stream(q8))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_fp8")
+    return out, lse
+
+
+def attn_decode_splits(B: int, H: int, H_kv: int, n_q: int, n_kv: int, d: int,
+                       num_splits: int = 0) -> int:
+    """Key ranges attn_fwd_decode uses on the current device (0 = its own choice)."""
+    rc = load_library().attn_decode_splits(B, H, H_kv, n_q, n_kv, d, d, int(num_splits))
+    if rc < 0:
+        raise AttnError(rc, "attn_decode_splits")
+    return rc
+
+
+def attn_fwd_decode(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+                    num_splits: int = 0, out=None, lse=None, workspace=None):
+    """Split-KV attention with grouped KV heads: q [B,H,N_q,d], k/v [B,H_kv,N_kv,d].
+
+    Returns O [B,H,N_q,d] (dtype of q) and LSE [B,H,N_q] float32. The workspace for
+    the split partials is allocated here (float32 tensor) unless one is passed.
+    """
+    import torch
+
+    _check(q, "q", (torch.bfloat16, torch.float16))
+    _check(k, "k", (q.dtype,))
+    _check(v, "v", (q.dtype,))
+    B, H, n_q, d = q.shape
+    H_kv, n_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, H_kv, n_kv, d) or v.shape != (B, H_kv, n_kv, v.shape[3]):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    d_v = v.shape[3]
+    if scale is None:
+        scale = d ** -0.5
+    lib = load_library()
+    splits = lib.attn_decode_splits(B, H, H_kv, n_q, n_kv, d, d_v, int(num_splits))
+    if splits < 0:
+        raise AttnError(splits, "attn_fwd_decode")
+    need = lib.attn_decode_workspace_bytes(B, H, n_q, d_v, splits)
+    if workspace is None and need:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
+    rc = lib.attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, n_q, n_kv,
+                             d, d_v, float(scale), int(bool(causal)), dtype, int(num_splits),
+                             _ptr(workspace), ws_bytes, _stream(q))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_decode")
     return out, lse

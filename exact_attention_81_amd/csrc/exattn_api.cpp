@@ -2,7 +2,9 @@
 // The contract of every entry point is documented in include/exattn.h.
 #include "exattn.h"
 
+#include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "launch.h"
@@ -67,6 +69,44 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// Split-KV decode: validation shared by attn_decode_splits and attn_fwd_decode.
+int check_decode(int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v) {
+  if (B < 1 || H < 1 || H_kv < 1 || N_q < 1 || N_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)(H / H_kv) * N_q > 128) return ATTN_ERR_SHAPE;
+  if (too_big(B, H, N_q, d_qk) || too_big(B, H_kv, N_kv, d_qk) || too_big(B, H_kv, N_kv, d_v) ||
+      too_big(B, H, N_q, d_v + 1))
+    return ATTN_ERR_SHAPE;
+  if (d_qk != d_v || (d_qk != 64 && d_qk != 128)) return ATTN_ERR_HEADDIM;
+  return ATTN_OK;
+}
+
+constexpr int kDecodeTile = 32;      // keys per decode tile
+constexpr int kDecodeMaxSplits = 256;
+
+// Keys per split for `splits` requested ranges: whole tiles, every range non-empty.
+int decode_chunk(int N_kv, int splits) {
+  const int tiles = (N_kv + kDecodeTile - 1) / kDecodeTile;
+  return (tiles + splits - 1) / splits * kDecodeTile;
+}
+
+// Split count for num_splits = 0: enough (batch, KV head, split) workgroups to give
+// every resident workgroup slot of the device one, but no split shorter than two
+// tiles per wave of a row block.
+int decode_auto_splits(int B, int H, int H_kv, int N_q, int N_kv, int d) {
+  const int slots = exattn::decode_resident_workgroups(d);
+  const int groups = B * H_kv;
+  if (slots <= 0 || groups >= slots) return 1;
+  const int rows = H / H_kv * N_q;
+  const int kv_waves = rows <= 32 ? 4 : rows <= 64 ? 2 : 1;  // waves sharing one row block
+  const int max_splits = std::max(1, N_kv / (2 * kDecodeTile * kv_waves));
+  return std::min({(slots + groups - 1) / groups, max_splits, kDecodeMaxSplits});
+}
+
+size_t decode_workspace(int B, int H, int N_q, int d_v, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * B * H * N_q * (size_t)(d_v + 1) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +165,59 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   p.Nkv = N_kv;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = exattn::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_decode_splits(int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v,
+                       int num_splits) {
+  if (int rc = check_decode(B, H, H_kv, N_q, N_kv, d_qk, d_v)) return rc;
+  if (num_splits < 0 || num_splits > kDecodeMaxSplits) return ATTN_ERR_ARG;
+  const int want = num_splits ? num_splits : decode_auto_splits(B, H, H_kv, N_q, N_kv, d_qk);
+  const int chunk = decode_chunk(N_kv, want);
+  return (N_kv + chunk - 1) / chunk;
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int N_q, int d_v, int splits) {
+  if (B < 1 || H < 1 || N_q < 1 || d_v < 1) return 0;
+  return decode_workspace(B, H, N_q, d_v, splits);
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int H_kv, int N_q, int N_kv, int d_qk, int d_v, float scale, int causal,
+                    int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (int rc = check_decode(B, H, H_kv, N_q, N_kv, d_qk, d_v)) return rc;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (workspace && !aligned16(workspace)))
+    return ATTN_ERR_ALIGN;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  const int splits = attn_decode_splits(B, H, H_kv, N_q, N_kv, d_qk, d_v, num_splits);
+  if (splits < 0) return splits;
+  const size_t need = decode_workspace(B, H, N_q, d_v, splits);
+  if (need && (!workspace || workspace_bytes < need)) return ATTN_ERR_ARG;
+  exattn::DecodeParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  if (need) {
+    p.o_part = static_cast<float*>(workspace);
+    p.lse_part = p.o_part + (size_t)splits * B * H * N_q * d_v;
+  }
+  p.B = B;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.splits = splits;
+  p.chunk = decode_chunk(N_kv, splits);
+  hipError_t e = exattn::launch_decode16(p, d_qk, causal != 0, dtype == ATTN_FP16,
+                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

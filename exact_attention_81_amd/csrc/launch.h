@@ -21,10 +21,29 @@ struct FwdParams {
   int n_qtiles;         // ceil(N_q / BLOCK_M)
 };
 
+// Arguments of one split-KV decode launch (16-bit inputs, grouped KV heads).
+struct DecodeParams {
+  const void* q;        // [B, H, N_q, d]
+  const void* k;        // [B, H_kv, N_kv, d]
+  const void* v;        // [B, H_kv, N_kv, d]
+  void* o;              // [B, H, N_q, d]
+  float* lse;           // [B, H, N_q]
+  float* o_part;        // splits > 1: [splits, B*H*N_q, d] fp32, O_s normalised by its own sum
+  float* lse_part;      // splits > 1: [splits, B*H*N_q] fp32
+  int B, H, Hkv, Nq, Nkv;
+  float scale_log2;     // softmax scale * log2(e), >= 0
+  int splits;           // key ranges per (batch, KV head)
+  int chunk;            // keys per range, a multiple of 32; splits * chunk >= N_kv
+};
+
 // Launchers (one per instantiation family); return hipError_t of the launch.
 hipError_t launch_fwd16(const FwdParams& p, int d_qk, int d_v, bool causal, bool fp16,
                         int tau, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, hipStream_t stream);
+hipError_t launch_decode16(const DecodeParams& p, int d, bool causal, bool fp16,
+                           hipStream_t stream);
+// Decode workgroups the current device runs at once for head dim d (0 if unknown).
+int decode_resident_workgroups(int d);
 hipError_t launch_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B, int H,
                                int N, const float* signs, bool transpose_out,
                                hipStream_t stream);

@@ -100,6 +100,51 @@ def qkv(B: int, H: int, N_q: int, N_kv: int, d_qk: int, d_v: int, seed: int,
     return q, k, v
 
 
+def qkv_gqa(B: int, H: int, H_kv: int, N_q: int, N_kv: int, d: int, seed: int,
+            dtype: torch.dtype = torch.bfloat16):
+    """Q [B,H,N_q,d], K and V [B,H_kv,N_kv,d] ~ N(0,1) (grouped KV heads), CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, N_q, d), generator=g, dtype=torch.float32).to(dtype)
+    k = torch.randn((B, H_kv, N_kv, d), generator=g, dtype=torch.float32).to(dtype)
+    v = torch.randn((B, H_kv, N_kv, d), generator=g, dtype=torch.float32).to(dtype)
+    return q, k, v
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """A decode-shaped problem: few queries per head, grouped KV heads, long keys."""
+
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    N_q: int
+    N_kv: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(self.d) ** -0.5
+
+    def hbm_bytes(self) -> int:
+        """Algorithmic HBM traffic of one call: K and V read once, Q read, O and LSE written."""
+        kv = 2 * self.B * self.H_kv * self.N_kv * self.d * 2
+        qo = 2 * self.B * self.H * self.N_q * self.d * 2
+        return kv + qo + 4 * self.B * self.H * self.N_q
+
+    def label(self) -> str:
+        c = "causal" if self.causal else "noncausal"
+        return (f"{self.name}:B{self.B}_H{self.H}_Hkv{self.H_kv}_Nq{self.N_q}_Nkv{self.N_kv}"
+                f"_d{self.d}_{c}_bf16")
+
+
+def decode_workload() -> DecodeWorkload:
+    """Single-token decode over a 16k-token cache with 8-way grouped KV heads."""
+    return DecodeWorkload("decode", 8, 64, 8, 1, 16384, 128, False, seed_for(6))
+
+
 def qkv_for(w: Workload, dtype: torch.dtype = torch.bfloat16):
     return qkv(w.B, w.H, w.N_q, w.N_kv, w.d_qk, w.d_v, w.seed, dtype)
 

@@ -30,6 +30,7 @@
 #ifndef EXATTN_H
 #define EXATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -135,6 +136,60 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
                  const float* q_descale, const float* k_descale, const float* v_descale,
                  void* o, float* lse, int B, int H, int N_q, int N_kv, int d_qk, int d_v,
                  float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_decode - split-KV attention forward for decode-shaped problems, with
+ * grouped KV heads ("Attention at Scale - From FlashAttention to
+ * FlashAttention-4", section "Beyond Training: Attention Kernels for Serving":
+ * decode is a few queries per head against a long key sequence; with grouped
+ * KV heads the key sequence is split across workgroups to occupy the GPU
+ * ("Sequence-Aware Split Heuristic"), and the partial results are combined by
+ * an associative merge ("FlashInfer")).
+ *
+ *   q    [B, H,    N_q,  d]  dtype    queries
+ *   k    [B, H_kv, N_kv, d]  dtype    keys
+ *   v    [B, H_kv, N_kv, d]  dtype    values
+ *   o    [B, H,    N_q,  d]  dtype    output, fully written (rounded to nearest even)
+ *   lse  [B, H,    N_q]      float32  natural-log logsumexp, as for attn_fwd
+ *   H_kv    KV heads; H must be a multiple of it. Query head h reads KV head
+ *           h / (H / H_kv) (consecutive query heads share a KV head).
+ *           (H / H_kv) * N_q must be at most 128, else ATTN_ERR_SHAPE.
+ *   d_qk = d_v = 64 or 128, else ATTN_ERR_HEADDIM.
+ *   scale, causal, dtype   as for attn_fwd (causal is bottom-right aligned).
+ *   num_splits  key ranges per (batch, KV head): 0 picks attn_decode_splits'
+ *           choice; 1..256 asks for that many (fewer are used when the key
+ *           sequence has fewer 32-key tiles). Other values: ATTN_ERR_ARG.
+ *   workspace   device memory of at least attn_decode_workspace_bytes(B, H, N_q,
+ *           d_v, s) bytes, 16-byte aligned, where s = attn_decode_splits(...);
+ *           may be NULL when s = 1. Too small or NULL otherwise: ATTN_ERR_ARG.
+ *           Its contents on entry do not matter; on return they are undefined.
+ *           Calls that share a workspace must not overlap in time.
+ *
+ * With s > 1 every split writes its fp32 partial (O normalised by its own sum,
+ * and its LSE) to the workspace and a second kernel merges them:
+ * LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v,
+                    float scale, int causal, int dtype, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_splits - the number of key ranges attn_fwd_decode uses for these
+ * arguments on the current device (num_splits = 0: its own choice, which gives
+ * every resident workgroup slot of the GPU one (batch, KV head, range) while
+ * keeping ranges at least two 32-key tiles per wave), or a negative error code
+ * for arguments attn_fwd_decode would reject.
+ */
+int attn_decode_splits(int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v,
+                       int num_splits);
+
+/*
+ * attn_decode_workspace_bytes - workspace attn_fwd_decode needs with `splits`
+ * key ranges: splits * B*H*N_q * (d_v + 1) * 4 bytes, 0 when splits <= 1 or a
+ * size is < 1.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int N_q, int d_v, int splits);
 
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -40,7 +40,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert names == ["attn_fwd", "attn_fwd_fp8", "attn_fwd_tau", "attn_quantize_fp8", "attn_strerror"]
+    assert names == ["attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd",
+                     "attn_fwd_decode", "attn_fwd_fp8", "attn_fwd_tau", "attn_quantize_fp8",
+                     "attn_strerror"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,6 +126,54 @@ def test_fwd_fp8_validation(lib):
     assert f(*a) == c["ATTN_ERR_ALIGN"]
     a = list(base); a[11] = 100
     assert f(*a) == c["ATTN_ERR_SHAPE"]
+
+
+def dec(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, Hkv=2, Nq=1, Nkv=4096, dqk=128, dv=128,
+             scale=0.1, causal=0, dtype=0, splits=4, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.attn_fwd_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                               a["Nq"], a["Nkv"], a["dqk"], a["dv"], a["scale"], a["causal"],
+                               a["dtype"], a["splits"], a["ws"], a["ws_bytes"], None)
+
+
+def test_attn_fwd_decode_validation(lib):
+    c = codes()
+    for name in ("q", "k", "v", "o", "lse"):
+        assert dec(lib, **{name: None}) == c["ATTN_ERR_NULL"]
+    for name in ("B", "H", "Hkv", "Nq", "Nkv"):
+        assert dec(lib, **{name: 0}) == c["ATTN_ERR_SHAPE"]
+    assert dec(lib, H=6, Hkv=4) == c["ATTN_ERR_SHAPE"]            # H not a multiple of H_kv
+    assert dec(lib, H=8, Hkv=1, Nq=17) == c["ATTN_ERR_SHAPE"]     # 8 * 17 = 136 rows > 128
+    for dqk, dv in ((192, 128), (64, 128), (96, 96)):
+        assert dec(lib, dqk=dqk, dv=dv) == c["ATTN_ERR_HEADDIM"]
+    assert dec(lib, dtype=3) == c["ATTN_ERR_DTYPE"]
+    assert dec(lib, scale=-1.0) == c["ATTN_ERR_SCALE"]
+    assert dec(lib, o=P + 4) == c["ATTN_ERR_ALIGN"]
+    assert dec(lib, ws=P + 4, ws_bytes=1 << 30) == c["ATTN_ERR_ALIGN"]
+    assert dec(lib, causal=2) == c["ATTN_ERR_ARG"]
+    assert dec(lib, splits=-1) == c["ATTN_ERR_ARG"]
+    assert dec(lib, splits=257) == c["ATTN_ERR_ARG"]
+    need = lib.attn_decode_workspace_bytes(2, 8, 1, 128, 4)
+    assert need == 4 * 2 * 8 * 1 * 129 * 4
+    assert dec(lib, ws=None) == c["ATTN_ERR_ARG"]                 # 4 splits need a workspace
+    assert dec(lib, ws=P, ws_bytes=need - 4) == c["ATTN_ERR_ARG"]
+
+
+def test_decode_split_count_and_workspace(lib):
+    c = codes()
+    s = lib.attn_decode_splits
+    assert s(2, 8, 2, 1, 4096, 128, 128, 4) == 4
+    assert s(2, 8, 2, 1, 4096, 128, 128, 1) == 1
+    assert s(1, 1, 1, 1, 100, 64, 64, 200) == 4       # only 4 tiles of 32 keys: 4 ranges
+    assert s(1, 1, 1, 1, 65, 64, 64, 2) == 2          # 3 tiles: ranges of 64 and 1 keys
+    assert s(1, 1, 1, 1, 64, 64, 64, 3) == 2          # 2 tiles: 2 ranges of 32 keys
+    auto = s(2, 8, 2, 1, 4096, 128, 128, 0)
+    assert 1 <= auto <= 256
+    assert s(1, 6, 4, 1, 64, 128, 128, 0) == c["ATTN_ERR_SHAPE"]
+    assert s(1, 8, 2, 1, 64, 128, 128, 300) == c["ATTN_ERR_ARG"]
+    assert lib.attn_decode_workspace_bytes(2, 8, 1, 128, 1) == 0
+    assert lib.attn_decode_workspace_bytes(0, 8, 1, 128, 4) == 0
 
 
 def test_binding_refuses_cpu_tensors():
