@@ -34,8 +34,9 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "device.h", "tile_io.h",
-                            "fp8_ops.h", "launch.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "device.h",
+                            "tile_io.h", "fp8_ops.h", "mfma16.h", "launch.h")]
+HBM_PEAK = 8000.0  # MI355X HBM3E, GB/s
 
 
 def kernel_source_hash() -> str:
@@ -89,6 +90,136 @@ def cpu_baseline(w_list, max_heads: int, min_seconds: float = 10.0):
                                         f"fork pool)"}
 
 
+def cpu_baseline_decode(w, max_heads: int, min_seconds: float = 10.0):
+    """Time the oracle on up to max_heads query heads of the decode workload (GB/s of the
+    call's algorithmic bytes, each query head counted as its share of them)."""
+    import oracle
+    from exact_attention_81_amd import synth
+
+    q, k, v = synth.qkv_gqa(w.B, w.H, w.H_kv, w.N_q, w.N_kv, w.d, w.seed)
+    q, k, v = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+    g = w.H // w.H_kv
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+    per_head = w.hbm_bytes() / (w.B * w.H)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for b, h in heads:
+            oracle.head(q[b, h], k[b, h // g], v[b, h // g], w.scale, w.causal)
+        done += len(heads)
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": per_head * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} query heads of {w.label()}, "
+                      f"{done // len(heads)} time(s) ({dt:.1f} s wall, float64 numpy, one process)"}
+
+
+def run_decode(args):
+    """Split-KV decode with grouped KV heads: one attn_fwd_decode call per step."""
+    from exact_attention_81_amd import synth
+
+    w = synth.decode_workload()
+    cpu = None if args.no_cpu_baseline else cpu_baseline_decode(w, args.cpu_heads)
+
+    import torch
+
+    import exact_attention_81_amd as ea
+
+    dev = torch.device("cuda:0")
+    q, k, v = synth.qkv_gqa(w.B, w.H, w.H_kv, w.N_q, w.N_kv, w.d, w.seed)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    splits = ea.attn_decode_splits(w.B, w.H, w.H_kv, w.N_q, w.N_kv, w.d)
+    o = torch.empty((w.B, w.H, w.N_q, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N_q), dtype=torch.float32, device=dev)
+    need = ea.load_library().attn_decode_workspace_bytes(w.B, w.H, w.N_q, w.d, splits)
+    ws = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev)
+
+    def launch():
+        ea.attn_fwd_decode(q, k, v, causal=w.causal, scale=w.scale, num_splits=splits, out=o,
+                           lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for e0, e1 in evs:
+        e0.record()
+        launch()
+        e1.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    cold = []
+    if args.cold_runs > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_runs):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    durs = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    avg_ms = sum(durs) / len(durs)
+    nbytes = w.hbm_bytes()
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    rec = {"variant": w.label(), "avg_launch_us": avg_ms * 1e3,
+           "median_launch_us": 0.5 * (durs[(len(durs) - 1) // 2] + durs[len(durs) // 2]) * 1e3,
+           "min_launch_us": durs[0] * 1e3, "gbps": achieved, "splits": splits}
+    if cold:
+        cavg = sum(cold) / len(cold)
+        rec["cold_avg_launch_us"] = cavg * 1e3
+        rec["cold_gbps"] = nbytes / (cavg * 1e-3) / 1e9
+    line = {
+        "metric": "attention decode (split-KV, grouped KV heads) HBM GB/s of K, V, Q, O, LSE",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q,K,V ~ N(0,1) rounded to bf16, seeded torch CPU generator",
+        "config": {"workload": w.label(), "B": w.B, "H": w.H, "H_kv": w.H_kv, "N_q": w.N_q,
+                   "N_kv": w.N_kv, "d": w.d, "causal": w.causal, "splits": splits,
+                   "step": "one attn_fwd_decode call (split kernel, then merge kernel)"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"attn_decode_kernel + merge_splits_kernel ({w.label()})",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK, 4),
+            "traffic": committed_traffic("decode"),
+        },
+        "per_variant": [rec],
+        "kernel_source_sha": kernel_source_hash(),
+        "wall_s_timed_region": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,7 +227,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="single",
                     choices=["single", "tiny", "asym", "fp8", "sweep512", "sweep1024",
-                             "sweep2048", "sweep4096", "sweep8192", "sweep16384"])
+                             "sweep2048", "sweep4096", "sweep8192", "sweep16384", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--cold-runs", type=int, default=5,
@@ -111,6 +242,10 @@ def main():
               f"forward is sharded by (batch, head) with no communication, so N GPUs would each "
               f"run this same one-GPU workload.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "decode":
+        run_decode(args)
+        return
 
     from exact_attention_81_amd import synth
 

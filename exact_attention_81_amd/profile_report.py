@@ -31,6 +31,8 @@ from . import synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_RE = re.compile(r"attn_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false)>")
 FP8_RE = re.compile(r"attn_fwd_fp8_kernel<(true|false)>")
+DEC_RE = re.compile(r"attn_decode_kernel<(\d+), (true|false), (true|false), (\d+)>")
+MERGE_RE = re.compile(r"merge_splits_kernel<(\d+), (true|false)>")
 
 
 def _one(pattern_dir: str, suffix: str) -> str:
@@ -49,6 +51,14 @@ def short_name(name: str) -> str:
     m = FP8_RE.search(name)
     if m:
         return f"attn_fwd_fp8_kernel d128x128 {'causal' if m.group(1) == 'true' else 'noncausal'} e4m3"
+    m = DEC_RE.search(name)
+    if m:
+        d, causal, f16, nrb = m.groups()
+        return (f"attn_decode_kernel d{d} {'causal' if causal == 'true' else 'noncausal'} "
+                f"{'fp16' if f16 == 'true' else 'bf16'} rowblocks{nrb}")
+    m = MERGE_RE.search(name)
+    if m:
+        return f"merge_splits_kernel d{m.group(1)} {'fp16' if m.group(2) == 'true' else 'bf16'}"
     if "quantize_kernel" in name:
         return "quantize_kernel (e4m3 prep)"
     if "neg" in name:
@@ -78,6 +88,8 @@ def counter_per_dispatch(d: str, counter: str):
 
 def algorithmic_bytes(w) -> int:
     """Q, K, V read once, O and LSE written once (fp8: 1-byte inputs plus descales)."""
+    if isinstance(w, synth.DecodeWorkload):
+        return w.hbm_bytes()
     bh = w.B * w.H
     ins = w.N_q * w.d_qk + w.N_kv * w.d_qk + w.N_kv * w.d_v
     if w.fp8:
@@ -87,6 +99,8 @@ def algorithmic_bytes(w) -> int:
 
 
 def workloads_of(name: str):
+    if name == "decode":
+        return [synth.decode_workload()]
     if name.startswith("sweep"):
         n = int(name[5:])
         return [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
@@ -97,6 +111,9 @@ def workloads_of(name: str):
 
 def variant_key(w) -> str:
     mask = "causal" if w.causal else "noncausal"
+    if isinstance(w, synth.DecodeWorkload):
+        rows = w.H // w.H_kv * w.N_q
+        return f"attn_decode_kernel d{w.d} {mask} bf16 rowblocks{1 if rows <= 32 else 2 if rows <= 64 else 4}"
     if w.fp8:
         return f"attn_fwd_fp8_kernel d128x128 {mask} e4m3"
     return f"attn_fwd_kernel d{w.d_qk}x{w.d_v} {mask} tau8 bf16"
@@ -138,9 +155,10 @@ def main():
         lines.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
                      f"{r['max_us']:.2f} | {r['pct']:.2f} |")
     lines += ["", "bench.py's HIP-event average of the same launches (the run under --stats):", "",
-              "| variant | avg us (events) | TFLOP/s |", "|---|---|---|"]
+              "| variant | avg us (events) | TFLOP/s (GB/s for decode) |", "|---|---|---|"]
     for p in bench["per_variant"]:
-        lines.append(f"| {p['variant']} | {p['avg_launch_us']:.2f} | {p['tflops']:.1f} |")
+        rate = f"{p['tflops']:.1f}" if "tflops" in p else f"{p['gbps']:.0f} GB/s"
+        lines.append(f"| {p['variant']} | {p['avg_launch_us']:.2f} | {rate} |")
     lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
               f"Calibration: a float32 copy of {args.copy_mib} MiB reads and writes {copy_bytes} bytes; "
               f"its FETCH_SIZE reads {fetch[copy_name][0]:.0f} KiB and WRITE_SIZE "

@@ -17,7 +17,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("workload", ["tiny", "fp8"])
+@pytest.mark.parametrize("workload", ["tiny", "fp8", "decode"])
 def test_bench_line(workload):
     print(f"[gpu-case] bench.py --workload {workload}", flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
@@ -32,8 +32,12 @@ def test_bench_line(workload):
     assert line["n_gpus"] == 1 and line["steps"] == 3 and line["warmup"] == 1
     assert line["value"] > 0 and line["ms_per_step"] > 0
     roof = line["roofline"]
-    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
-    assert roof["peak"] == (5000.0 if workload == "fp8" else 2500.0)
+    if workload == "decode":
+        assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+        assert line["unit"] == "GB/s" and line["config"]["splits"] >= 1
+    else:
+        assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+        assert roof["peak"] == (5000.0 if workload == "fp8" else 2500.0)
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert "workload" in line["config"]
     for p in line["per_variant"]:

@@ -24,9 +24,20 @@ def test_short_names():
         "void exattn::(anonymous namespace)::attn_fwd_fp8_kernel<false>(exattn::FwdParams)") == \
         "attn_fwd_fp8_kernel d128x128 noncausal e4m3"
     assert profile_report.short_name(COPY) == "copy (torch.neg, float32)"
+    assert profile_report.short_name(
+        "void exattn::(anonymous namespace)::attn_decode_kernel<128, false, false, 1>"
+        "(exattn::DecodeParams)") == "attn_decode_kernel d128 noncausal bf16 rowblocks1"
+    assert profile_report.short_name(
+        "void exattn::(anonymous namespace)::merge_splits_kernel<64, true>(float const*, "
+        "float const*, void*, float*, int, int)") == "merge_splits_kernel d64 fp16"
+    w = synth.decode_workload()
+    assert profile_report.variant_key(w) == "attn_decode_kernel d128 noncausal bf16 rowblocks1"
 
 
 def test_algorithmic_bytes():
+    dw = synth.decode_workload()
+    assert profile_report.algorithmic_bytes(dw) == (2 * 8 * 8 * 16384 * 128 * 2
+                                                    + 2 * 8 * 64 * 1 * 128 * 2 + 4 * 8 * 64)
     w = synth.workload("single", causal=False)
     assert profile_report.algorithmic_bytes(w) == 4 * 16 * (2048 * 128 * 2 * 4 + 2048 * 4)
     f = synth.workload("fp8")
