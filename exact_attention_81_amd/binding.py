@@ -49,6 +49,10 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_fwd.restype = i
     lib.attn_fwd_tau.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i64p, i64p,
+                                     f, i, i, vp]
+    lib.attn_fwd_strided.restype = i
     lib.attn_fwd_tau.restype = i
     lib.attn_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, vp, i, vp]
     lib.attn_quantize_fp8.restype = i
@@ -92,9 +96,29 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _check_strided(t, name, dtypes):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must be dense along its last dimension")
+
+
+def _strides(t):
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
 def _fwd(q, k, v, causal, scale, tau, out, lse):
     import torch
 
+    dense = all(t.is_contiguous() for t in (q, k, v)) and (out is None or out.is_contiguous())
+    if not dense:
+        if tau is not None:
+            raise ValueError("attn_fwd_tau takes contiguous tensors")
+        return _fwd_strided(q, k, v, causal, scale, out, lse)
     _check(q, "q", (torch.bfloat16, torch.float16))
     _check(k, "k", (q.dtype,))
     _check(v, "v", (q.dtype,))
@@ -123,9 +147,41 @@ def _fwd(q, k, v, causal, scale, tau, out, lse):
     return out, lse
 
 
+def _fwd_strided(q, k, v, causal, scale, out, lse):
+    import torch
+
+    _check_strided(q, "q", (torch.bfloat16, torch.float16))
+    _check_strided(k, "k", (q.dtype,))
+    _check_strided(v, "v", (q.dtype,))
+    B, H, n_q, d_qk = q.shape
+    n_kv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, n_kv, d_qk) or v.shape != (B, H, n_kv, d_v):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = d_qk ** -0.5
+    if out is None:
+        out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    _check_strided(out, "out", (q.dtype,))
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
+    rc = load_library().attn_fwd_strided(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_kv, d_qk, d_v,
+        _strides(q), _strides(k), _strides(v), _strides(out), float(scale), int(bool(causal)),
+        dtype, _stream(q))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_strided")
+    return out, lse
+
+
 def attn_fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
              out=None, lse=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """O [B,H,N_q,d_v] (dtype of q) and LSE [B,H,N_q] float32."""
+    """O [B,H,N_q,d_v] (dtype of q) and LSE [B,H,N_q] float32.
+
+    Contiguous [B,H,N,d] tensors go to attn_fwd; any other layout whose last dimension
+    is dense (e.g. a [B,N,H,d] buffer viewed as [B,H,N,d]) to attn_fwd_strided. ``out``
+    may be such a view too.
+    """
     return _fwd(q, k, v, causal, scale, None, out, lse)
 
 

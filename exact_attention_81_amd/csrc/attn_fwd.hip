@@ -51,7 +51,7 @@ constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int ROWS_PER_WAVE = BLOCK_M / NWAVES;  // 32: one MFMA column block
 
-template <int DQK, int DV, bool CAUSAL, int TAU, bool F16>
+template <int DQK, int DV, bool CAUSAL, int TAU, bool F16, bool STRIDED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const FwdParams p) {
@@ -96,9 +96,18 @@ void attn_fwd_kernel(const FwdParams p) {
   const int q0 = qt * BLOCK_M;
   const int offset = p.Nkv - p.Nq;  // causal: key j visible to query i iff j <= i + offset
 
-  const uint8_t* __restrict__ qg = (const uint8_t*)p.q + (size_t)bh * p.Nq * DQK * 2;
-  const uint8_t* __restrict__ kg = (const uint8_t*)p.k + (size_t)bh * p.Nkv * DQK * 2;
-  const uint8_t* __restrict__ vg = (const uint8_t*)p.v + (size_t)bh * p.Nkv * DV * 2;
+  // Dense BHND, or (STRIDED) element strides along batch, head and row with a dense
+  // last dimension. Bytes per row of each tensor:
+  const int q_row = STRIDED ? p.q_sn * 2 : DQK * 2;
+  const int k_row = STRIDED ? p.k_sn * 2 : DQK * 2;
+  const int v_row = STRIDED ? p.v_sn * 2 : DV * 2;
+  const int b_ = bh / p.H, h_ = bh - b_ * p.H;
+  auto base = [&](const void* t, long long sb, long long sh, int rows, int d) {
+    return (const uint8_t*)t + (STRIDED ? (b_ * sb + h_ * sh) * 2 : (size_t)bh * rows * d * 2);
+  };
+  const uint8_t* __restrict__ qg = base(p.q, p.q_sb, p.q_sh, p.Nq, DQK);
+  const uint8_t* __restrict__ kg = base(p.k, p.k_sb, p.k_sh, p.Nkv, DQK);
+  const uint8_t* __restrict__ vg = base(p.v, p.v_sb, p.v_sh, p.Nkv, DV);
 
   int kv_end = p.Nkv;
   if (CAUSAL) kv_end = min(p.Nkv, max(0, q0 + BLOCK_M + offset));
@@ -111,7 +120,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     u32x4_t x = {0u, 0u, 0u, 0u};
-    if (my_q < p.Nq) x = *(const u32x4_t*)(qg + (size_t)my_q * DQK * 2 + s * 32 + half * 16);
+    if (my_q < p.Nq) x = *(const u32x4_t*)(qg + (size_t)my_q * q_row + s * 32 + half * 16);
     qf[s] = x;
   }
 
@@ -132,20 +141,20 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int rows_per = 1024 / KA_ROW, cpr = KA_ROW / 16;
     const int i = wave + t * NWAVES;
     const int r = i * rows_per + lane / cpr;
-    ka_off[t] = r * DQK * 2 + k_swz(lane % cpr, r, KA_W16) * 16;
+    ka_off[t] = r * k_row + k_swz(lane % cpr, r, KA_W16) * 16;
   }
 #pragma unroll
   for (int t = 0; t < KB_PER; ++t) {
     const int i = wave + t * NWAVES;
     const int r = i * 8 + lane / 8;
-    kb_off[t] = r * DQK * 2 + KA_ROW + k_swz(lane % 8, r, false) * 16;
+    kb_off[t] = r * k_row + KA_ROW + k_swz(lane % 8, r, false) * 16;
   }
 #pragma unroll
   for (int t = 0; t < V_PER; ++t) {
     constexpr int rows_per = 1024 / V_ROW, cpr = V_ROW / 16;
     const int i = wave + t * NWAVES;
     const int r = i * rows_per + lane / cpr;
-    v_off[t] = r * V_ROW + v_swz(lane % cpr, r, V_W16) * 16;
+    v_off[t] = r * v_row + v_swz(lane % cpr, r, V_W16) * 16;
   }
   // Tiles past the last one are still "loaded" through an empty resource (every lane
   // reads zero bytes), which keeps the number of loads in flight the same at every
@@ -154,7 +163,7 @@ void attn_fwd_kernel(const FwdParams p) {
   // below is a per-lane register plus an immediate offset.
   auto issue_k = [&](int j, auto stage) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * DQK * 2, (p.Nkv - key0) * DQK * 2);
+    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * k_row, (p.Nkv - key0) * k_row);
     lds_u8* st = k_lds + int(stage) * K_STAGE;
 #pragma unroll
     for (int t = 0; t < KA_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, ka_off[t]);
@@ -164,7 +173,7 @@ void attn_fwd_kernel(const FwdParams p) {
   };
   auto issue_v = [&](int j, auto stage) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * DV * 2, (p.Nkv - key0) * DV * 2);
+    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * v_row, (p.Nkv - key0) * v_row);
     lds_u8* st = v_lds + int(stage) * V_STAGE;
 #pragma unroll
     for (int t = 0; t < V_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, v_off[t]);
@@ -372,9 +381,9 @@ void attn_fwd_kernel(const FwdParams p) {
   static_assert(ISSUE_GAP >= 1, "one load per PV product at most");
   auto spread_issue = [&](int j, auto k_next, auto v_next) {
     const int kkey0 = min((j + 2) * BLOCK_N, p.Nkv);
-    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * DQK * 2, (p.Nkv - kkey0) * DQK * 2);
+    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * k_row, (p.Nkv - kkey0) * k_row);
     const int vkey0 = min((j + 1) * BLOCK_N, p.Nkv);
-    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * DV * 2, (p.Nkv - vkey0) * DV * 2);
+    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * v_row, (p.Nkv - vkey0) * v_row);
     lds_u8* kst = k_lds + int(k_next) * K_STAGE;
     lds_u8* vst = v_lds + int(v_next) * V_STAGE;
     return [=](int step) {
@@ -466,7 +475,9 @@ void attn_fwd_kernel(const FwdParams p) {
   const bool any = l > 0.f;
   const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
   if (my_q < p.Nq) {
-    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * DV * 2;
+    uint8_t* __restrict__ og =
+        STRIDED ? (uint8_t*)p.o + (b_ * p.o_sb + h_ * p.o_sh + (long long)my_q * p.o_sn) * 2
+                : (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * DV * 2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -481,11 +492,28 @@ void attn_fwd_kernel(const FwdParams p) {
   }
 }
 
+// Dense BHND tensors run the kernel with compile-time row sizes; other strides (only
+// with the default rescale threshold) run the STRIDED instance.
+bool is_dense(const FwdParams& p, int dqk, int dv) {
+  const long long rq = p.Nq, rk = p.Nkv;
+  return p.q_sn == dqk && p.k_sn == dqk && p.v_sn == dv && p.o_sn == dv && p.q_sh == rq * dqk &&
+         p.k_sh == rk * dqk && p.v_sh == rk * dv && p.o_sh == rq * dv &&
+         p.q_sb == p.H * rq * dqk && p.k_sb == p.H * rk * dqk && p.v_sb == p.H * rk * dv &&
+         p.o_sb == p.H * rq * dv;
+}
+
 template <int DQK, int DV, bool CAUSAL, int TAU, bool F16>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int grid = p.n_qtiles * p.B * p.H;
-  hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, CAUSAL, TAU, F16>), dim3(grid), dim3(NTHREADS), 0,
-                     stream, p);
+  if (is_dense(p, DQK, DV)) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, CAUSAL, TAU, F16, false>), dim3(grid),
+                       dim3(NTHREADS), 0, stream, p);
+  } else if constexpr (TAU == 8) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, CAUSAL, TAU, F16, true>), dim3(grid),
+                       dim3(NTHREADS), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

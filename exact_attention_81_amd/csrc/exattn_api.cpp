@@ -42,18 +42,66 @@ int check_scale(float scale) {
   return (std::isfinite(scale) && scale >= 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
 }
 
+// Element strides (batch, head, row) of the four 16-bit tensors, in the order q, k, v, o.
+struct Strides16 {
+  int64_t v[4][3];
+};
+
+Strides16 dense_strides(int H, int N_q, int N_kv, int d_qk, int d_v) {
+  Strides16 st;
+  const int64_t rows[4] = {N_q, N_kv, N_kv, N_q};
+  const int64_t dims[4] = {d_qk, d_qk, d_v, d_v};
+  for (int t = 0; t < 4; ++t) {
+    st.v[t][2] = dims[t];
+    st.v[t][1] = rows[t] * dims[t];
+    st.v[t][0] = H * rows[t] * dims[t];
+  }
+  return st;
+}
+
+// Shape checks of a strided call: every stride >= 0, rows at least d elements apart,
+// row offsets of a (batch, head) slice below 2^30 elements (32-bit byte offsets).
+int check_strides_shape(const Strides16& st, int N_q, int N_kv, int d_qk, int d_v) {
+  const int64_t rows[4] = {N_q, N_kv, N_kv, N_q};
+  const int64_t dims[4] = {d_qk, d_qk, d_v, d_v};
+  for (int t = 0; t < 4; ++t) {
+    if (st.v[t][0] < 0 || st.v[t][1] < 0 || st.v[t][2] < dims[t]) return ATTN_ERR_SHAPE;
+    if (st.v[t][2] * rows[t] >= (int64_t(1) << 30)) return ATTN_ERR_SHAPE;
+    if (st.v[t][0] >= (int64_t(1) << 40) || st.v[t][1] >= (int64_t(1) << 40)) return ATTN_ERR_SHAPE;
+  }
+  return ATTN_OK;
+}
+
+// 16-byte loads and stores need every stride to be a multiple of 8 elements.
+bool strides_aligned(const Strides16& st) {
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i)
+      if (st.v[t][i] % 8) return false;
+  return true;
+}
+
 int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N_q,
-          int N_kv, int d_qk, int d_v, float scale, int causal, int dtype, int tau, void* stream) {
+          int N_kv, int d_qk, int d_v, float scale, int causal, int dtype, int tau,
+          const Strides16* strided, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (int rc = check_shape(B, H, N_q, N_kv, d_qk, d_v)) return rc;
+  const Strides16 st = strided ? *strided : dense_strides(H, N_q, N_kv, d_qk, d_v);
+  if (strided) {
+    if (int rc = check_strides_shape(st, N_q, N_kv, d_qk, d_v)) return rc;
+  }
   if (!supported_dims16(d_qk, d_v)) return ATTN_ERR_HEADDIM;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
   if (int rc = check_scale(scale)) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !strides_aligned(st))
     return ATTN_ERR_ALIGN;
   if (tau != 0 && tau != 8) return ATTN_ERR_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
   FwdParams p = {};
+  p.q_sb = st.v[0][0], p.q_sh = st.v[0][1], p.q_sn = (int)st.v[0][2];
+  p.k_sb = st.v[1][0], p.k_sh = st.v[1][1], p.k_sn = (int)st.v[1][2];
+  p.v_sb = st.v[2][0], p.v_sh = st.v[2][1], p.v_sn = (int)st.v[2][2];
+  p.o_sb = st.v[3][0], p.o_sh = st.v[3][1], p.o_sn = (int)st.v[3][2];
   p.q = q;
   p.k = k;
   p.v = v;
@@ -114,14 +162,27 @@ extern "C" {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int N_q, int N_kv, int d_qk, int d_v, float scale, int causal, int dtype,
              void* stream) {
-  return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, 8, stream);
+  return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, 8, nullptr,
+               stream);
+}
+
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N_q, int N_kv, int d_qk, int d_v, const int64_t* q_strides,
+                     const int64_t* k_strides, const int64_t* v_strides,
+                     const int64_t* o_strides, float scale, int causal, int dtype, void* stream) {
+  if (!q_strides || !k_strides || !v_strides || !o_strides) return ATTN_ERR_NULL;
+  Strides16 st;
+  const int64_t* src[4] = {q_strides, k_strides, v_strides, o_strides};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) st.v[t][i] = src[t][i];
+  return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, 8, &st, stream);
 }
 
 int attn_fwd_tau(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N_q, int N_kv, int d_qk, int d_v, float scale, int causal, int dtype,
                  int tau_log2, void* stream) {
   return fwd16(q, k, v, o, lse, B, H, N_q, N_kv, d_qk, d_v, scale, causal, dtype, tau_log2,
-               stream);
+               nullptr, stream);
 }
 
 int attn_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B, int H, int N, int d,

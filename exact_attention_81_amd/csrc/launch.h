@@ -19,6 +19,11 @@ struct FwdParams {
   int B, H, Nq, Nkv;
   float scale_log2;     // softmax scale * log2(e), >= 0
   int n_qtiles;         // ceil(N_q / BLOCK_M)
+  // 16-bit path: element strides of Q, K, V and O along batch, head and row (the last
+  // dim is dense). Row strides times N are below 2^30, so byte offsets of rows fit in
+  // 32 bits. The fp8 path reads dense BHND and ignores them.
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sn, k_sn, v_sn, o_sn;
 };
 
 // Arguments of one split-KV decode launch (16-bit inputs, grouped KV heads).

@@ -29,7 +29,8 @@ from collections import defaultdict
 from . import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_RE = re.compile(r"attn_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false)>")
+KERNEL_RE = re.compile(
+    r"attn_fwd_kernel<(\d+), (\d+), (true|false), (\d+), (true|false)(?:, (true|false))?>")
 FP8_RE = re.compile(r"attn_fwd_fp8_kernel<(true|false)>")
 DEC_RE = re.compile(r"attn_decode_kernel<(\d+), (true|false), (true|false), (\d+)>")
 MERGE_RE = re.compile(r"merge_splits_kernel<(\d+), (true|false)>")
@@ -45,9 +46,10 @@ def _one(pattern_dir: str, suffix: str) -> str:
 def short_name(name: str) -> str:
     m = KERNEL_RE.search(name)
     if m:
-        dqk, dv, causal, tau, f16 = m.groups()
+        dqk, dv, causal, tau, f16, strided = m.groups()
         return (f"attn_fwd_kernel d{dqk}x{dv} {'causal' if causal == 'true' else 'noncausal'} "
-                f"tau{tau} {'fp16' if f16 == 'true' else 'bf16'}")
+                f"tau{tau} {'fp16' if f16 == 'true' else 'bf16'}"
+                f"{' strided' if strided == 'true' else ''}")
     m = FP8_RE.search(name)
     if m:
         return f"attn_fwd_fp8_kernel d128x128 {'causal' if m.group(1) == 'true' else 'noncausal'} e4m3"

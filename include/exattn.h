@@ -85,6 +85,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_fwd_strided - attn_fwd on tensors with arbitrary element strides, e.g. the
+ * [B, N, H, d] ("BNHD") layout or a view into a larger buffer. The layout is an
+ * interface matter the pages leave open; the arithmetic is attn_fwd's.
+ *
+ *   q_strides, k_strides, v_strides, o_strides  host pointers to 3 int64 each: the
+ *           element strides along batch, head and row of q, k, v and o; the last
+ *           dimension is dense (stride 1). Dense BHND is {H*N*d, N*d, d}.
+ *   Every stride must be >= 0, row strides at least the row length (d_qk for q and
+ *   k, d_v for v and o) and row stride * N below 2^30, batch and head strides below
+ *   2^40 (else ATTN_ERR_SHAPE); every stride a multiple of 8 elements (16 bytes, else
+ *   ATTN_ERR_ALIGN). lse stays dense [B, H, N_q]. o must not overlap q, k, v or lse.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N_q, int N_kv, int d_qk, int d_v,
+                     const int64_t* q_strides, const int64_t* k_strides,
+                     const int64_t* v_strides, const int64_t* o_strides,
+                     float scale, int causal, int dtype, void* stream);
+
+/*
  * attn_fwd_tau - attn_fwd with an explicit rescale threshold, for checking
  * that the conditional rescale leaves the result unchanged.
  *   tau_log2  0: refresh the row maximum whenever it grows (plain online

@@ -41,8 +41,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert names == ["attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd",
-                     "attn_fwd_decode", "attn_fwd_fp8", "attn_fwd_tau", "attn_quantize_fp8",
-                     "attn_strerror"]
+                     "attn_fwd_decode", "attn_fwd_fp8", "attn_fwd_strided", "attn_fwd_tau",
+                     "attn_quantize_fp8", "attn_strerror"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -126,6 +126,39 @@ def test_fwd_fp8_validation(lib):
     assert f(*a) == c["ATTN_ERR_ALIGN"]
     a = list(base); a[11] = 100
     assert f(*a) == c["ATTN_ERR_SHAPE"]
+
+
+def strided(lib, qs=None, ks=None, vs=None, os_=None, **kw):
+    import ctypes as C
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Nq=64, Nkv=64, dqk=128, dv=128, scale=0.1,
+             causal=0, dtype=0)
+    a.update(kw)
+    dense = lambda n, d: [a["H"] * n * d, n * d, d]
+    arr = lambda x: None if x is False else (C.c_int64 * 3)(*x)
+    return lib.attn_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                a["Nkv"], a["dqk"], a["dv"],
+                                arr(qs if qs is not None else dense(a["Nq"], a["dqk"])),
+                                arr(ks if ks is not None else dense(a["Nkv"], a["dqk"])),
+                                arr(vs if vs is not None else dense(a["Nkv"], a["dv"])),
+                                arr(os_ if os_ is not None else dense(a["Nq"], a["dv"])),
+                                a["scale"], a["causal"], a["dtype"], None)
+
+
+def test_attn_fwd_strided_validation(lib):
+    c = codes()
+    assert strided(lib, q=None) == c["ATTN_ERR_NULL"]
+    assert strided(lib, qs=False) == c["ATTN_ERR_NULL"]
+    assert strided(lib, os_=False) == c["ATTN_ERR_NULL"]
+    assert strided(lib, qs=[-8, 8192, 128]) == c["ATTN_ERR_SHAPE"]        # negative stride
+    assert strided(lib, ks=[32768, 8192, 64]) == c["ATTN_ERR_SHAPE"]      # rows overlap
+    assert strided(lib, vs=[0, 0, 1 << 24]) == c["ATTN_ERR_SHAPE"]        # row offsets >= 2^30
+    assert strided(lib, ks=[1 << 41, 8192, 128]) == c["ATTN_ERR_SHAPE"]
+    assert strided(lib, dqk=96, dv=96) == c["ATTN_ERR_HEADDIM"]
+    assert strided(lib, dtype=5) == c["ATTN_ERR_DTYPE"]
+    assert strided(lib, scale=-2.0) == c["ATTN_ERR_SCALE"]
+    assert strided(lib, qs=[32768, 8192, 132]) == c["ATTN_ERR_ALIGN"]     # 264-byte rows
+    assert strided(lib, os_=[32772, 8192, 128]) == c["ATTN_ERR_ALIGN"]
+    assert strided(lib, causal=3) == c["ATTN_ERR_ARG"]
 
 
 def dec(lib, **kw):

@@ -1,0 +1,84 @@
+"""GPU parity of attn_fwd on strided tensors (attn_fwd_strided) against the float64 oracle.
+
+The oracle reads the same values from contiguous copies; the kernel reads them through
+views whose batch, head and row strides differ from dense [B, H, N, d].
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_81_amd as ea
+import oracle
+from exact_attention_81_amd import synth
+from gpu_util import compare, f64, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def bnhd(t, dev):
+    """The same values stored [B, N, H, d], viewed as [B, H, N, d]."""
+    return t.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+
+
+def padded(t, dev, pad=8):
+    """The same values in rows padded by `pad` elements, viewed as [B, H, N, d]."""
+    B, H, N, d = t.shape
+    buf = torch.zeros((B, H, N, d + pad), dtype=t.dtype, device=dev)
+    buf[..., :d] = t.to(dev)
+    return buf[..., :d]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 300, 300, 128, 128), (1, 3, 129, 513, 64, 64),
+                                   (2, 2, 257, 255, 192, 128)],
+                         ids=lambda s: "B{}H{}_{}x{}_d{}x{}".format(*s))
+def test_bnhd_inputs_and_output(shape, causal):
+    B, H, nq, nkv, dqk, dv = shape
+    dev = require_gpu()
+    q, k, v = synth.qkv(B, H, nq, nkv, dqk, dv, seed=nq + nkv + dqk + int(causal))
+    label = f"BNHD B{B} H{H} Nq{nq} Nkv{nkv} d{dqk}x{dv} causal={causal}"
+    log("start " + label)
+    qs, ks, vs = bnhd(q, dev), bnhd(k, dev), bnhd(v, dev)
+    assert not qs.is_contiguous()
+    out = torch.empty((B, nq, H, dv), dtype=q.dtype, device=dev).permute(0, 2, 1, 3)
+    o, lse = ea.attn_fwd(qs, ks, vs, causal=causal, out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    o_ref, lse_ref = oracle.attention(q, k, v, dqk ** -0.5, causal)
+    compare(f64(o), f64(lse), o_ref, lse_ref, label)
+    # the same call on dense tensors gives the same bits
+    o2, lse2 = ea.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o2) and torch.equal(lse, lse2)
+
+
+def test_padded_rows_and_packed_kv():
+    dev = require_gpu()
+    B, H, nq, nkv, d = 2, 4, 200, 333, 128
+    q, k, v = synth.qkv(B, H, nq, nkv, d, d, seed=77)
+    log("start padded rows")
+    o, lse = ea.attn_fwd(padded(q, dev), padded(k, dev, 16), padded(v, dev, 24), causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, d ** -0.5, True)
+    compare(f64(o), f64(lse), o_ref, lse_ref, "padded rows")
+    log("start packed kv [B, N, 2, H, d]")
+    kv = torch.stack([k, v], dim=2).permute(0, 3, 2, 1, 4).contiguous().to(dev)  # B N 2 H d
+    kk = kv[:, :, 0].permute(0, 2, 1, 3)
+    vv = kv[:, :, 1].permute(0, 2, 1, 3)
+    assert kk.stride() == (nkv * 2 * H * d, d, 2 * H * d, 1)
+    o, lse = ea.attn_fwd(q.to(dev), kk, vv, causal=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, d ** -0.5, False)
+    compare(f64(o), f64(lse), o_ref, lse_ref, "packed kv")
+
+
+def test_strided_rejects_bad_views():
+    dev = require_gpu()
+    q, k, v = synth.qkv(1, 2, 64, 64, 128, 128, seed=78)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q.transpose(2, 3), k, v)           # last dimension not dense
+    odd = torch.zeros((1, 2, 64, 132), dtype=q.dtype, device=dev)[..., :128]
+    with pytest.raises(ea.AttnError):                  # 264-byte rows: not 16-byte aligned
+        ea.attn_fwd(odd, k, v)
+    np.testing.assert_equal(ea.attn_strerror(-6), "tensor pointer not 16-byte aligned")

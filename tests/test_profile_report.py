@@ -5,7 +5,7 @@ import os
 
 from exact_attention_81_amd import profile_report, synth
 
-KNAME = "void exattn::(anonymous namespace)::attn_fwd_kernel<128, 128, {c}, 8, false>(exattn::FwdParams)"
+KNAME = "void exattn::(anonymous namespace)::attn_fwd_kernel<128, 128, {c}, 8, false, false>(exattn::FwdParams)"
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>(...)"
 
 
@@ -24,6 +24,8 @@ def test_short_names():
         "void exattn::(anonymous namespace)::attn_fwd_fp8_kernel<false>(exattn::FwdParams)") == \
         "attn_fwd_fp8_kernel d128x128 noncausal e4m3"
     assert profile_report.short_name(COPY) == "copy (torch.neg, float32)"
+    assert profile_report.short_name(KNAME.replace("false, false>", "false, true>").format(c="false")) \
+        == "attn_fwd_kernel d128x128 noncausal tau8 bf16 strided"
     assert profile_report.short_name(
         "void exattn::(anonymous namespace)::attn_decode_kernel<128, false, false, 1>"
         "(exattn::DecodeParams)") == "attn_decode_kernel d128 noncausal bf16 rowblocks1"
