@@ -17,3 +17,4 @@ from .fp8 import (  # noqa: F401
     rotation,
 )
 from .decode import attention_gqa, head_keys, kv_head, merge  # noqa: F401
+from .backward import attention_backward, head_backward  # noqa: F401
