@@ -8,6 +8,7 @@ the library has not been built.
 """
 from .binding import (  # noqa: F401
     AttnError,
+    attn_bwd,
     attn_decode_splits,
     attn_fwd,
     attn_fwd_decode,

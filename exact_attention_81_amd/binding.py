@@ -65,6 +65,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_decode_splits.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.attn_bwd.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -289,3 +291,29 @@ def attn_fwd_decode(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     if rc != 0:
         raise AttnError(rc, "attn_fwd_decode")
     return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None):
+    """dQ, dK, dV (dtype of q) of attn_fwd's output o / lse for the upstream gradient dout."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(t, name, (torch.bfloat16, torch.float16) if name == "q" else (q.dtype,))
+    if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    B, H, n_q, d = q.shape
+    n_kv = k.shape[2]
+    if k.shape != (B, H, n_kv, d) or v.shape != (B, H, n_kv, d) or o.shape != q.shape or \
+            dout.shape != q.shape or lse.shape != (B, H, n_q):
+        raise ValueError("shape mismatch between q, k, v, o, dout and lse")
+    if scale is None:
+        scale = d ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
+    rc = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, H, n_q, n_kv, d, d,
+                                 float(scale), int(bool(causal)), dtype, _stream(q))
+    if rc != 0:
+        raise AttnError(rc, "attn_bwd")
+    return dq, dk, dv

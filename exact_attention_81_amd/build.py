@@ -23,7 +23,7 @@ LIB_NAME = "libexattn.so"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_fp8.hip", "attn_decode.hip"]
+HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_fp8.hip", "attn_decode.hip", "attn_bwd.hip"]
 HOST_SOURCES = ["exattn_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",

@@ -1,0 +1,411 @@
+// Attention backward on gfx950 (MI355X), bf16 / fp16: dQ, dK, dV from Q, K, V, O, dO
+// and the forward's LSE.
+//
+// The gradient of one (b, h) is five matrix products and two elementwise steps
+// ("FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for Asymmetric
+// Hardware Scaling", Figure 2; "FlashAttention 3 and 4: When the Bottleneck
+// Moves", section 3.2, the backward-pass paragraph): with the scores recomputed
+// from Q, K and the saved LSE, P = exp(scale Q K^T - LSE),
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,
+//     dK = scale dS^T Q,   D_i = sum_c dO_ic O_ic.
+// Two kernels, no atomics, so every result is deterministic:
+//   * attn_bwd_dq_kernel: one workgroup per 128 query rows streams the K/V tiles
+//     (S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T) and also writes D;
+//   * attn_bwd_dkdv_kernel: one workgroup per 128 keys streams 32-query tiles of
+//     Q, dO, LSE and D (S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS).
+// Products are 32x32x16 MFMAs with the operand layouts of the forward kernel: a
+// 16-byte piece of a row per lane for row operands, transposing LDS reads for
+// the transposed ones, and P / dS fed from the accumulator registers in the
+// row order the transposing reads reproduce. Tiles go straight from global memory
+// into LDS (buffer_load ... lds), double-buffered, one workgroup barrier per tile.
+#include "device.h"
+#include "mfma16.h"
+#include "tile_io.h"
+
+namespace exattn {
+namespace {
+
+constexpr int BW_WAVES = 4;
+constexpr int BW_THREADS = 64 * BW_WAVES;
+
+// Row-major tile of R rows x D 16-bit values in LDS, 16-byte chunks XOR-swizzled by
+// k_swz. Reads: a row piece (A or B operand of a product over D), or, through the
+// transposing read, a block of the transposed tile (A operand of a product over the
+// tile's rows, rows in the order of the MFMA accumulator rows).
+template <int D>
+struct SwzTile {
+  static constexpr int ROW = D * 2;
+  static constexpr bool W16 = D == 128;
+  // Byte offset of chunk c (16 bytes) of row r.
+  static __device__ int at(int r, int c) { return r * ROW + k_swz(c, r, W16) * 16; }
+};
+
+// Direct-to-LDS load of rows [row0, row0 + R) of a [N, D] 16-bit matrix at `base`
+// (rows past N read as zeros) into an LDS tile; the waves of the workgroup share the
+// 1 KB instructions: instruction i fills LDS bytes [1024 i, 1024 i + 1024), lane l
+// writes the 16 bytes at 1024 i + 16 l, so it loads the chunk that belongs there.
+template <int D, int R>
+__device__ inline void load_tile(lds_u8* dst, const uint8_t* base, int row0, int N, int wave, int lane) {
+  constexpr int ROW = D * 2, NI = R * ROW / 1024, ROWS_PER = 1024 / ROW, CPR = ROW / 16;
+  static_assert(NI % BW_WAVES == 0, "every wave issues the same number of loads");
+  const int r0 = min(row0, N);
+  const i32x4_t rs = make_rsrc(base + (size_t)r0 * ROW, (N - r0) * ROW);
+#pragma unroll
+  for (int t = 0; t < NI / BW_WAVES; ++t) {
+    const int i = wave + t * BW_WAVES;
+    const int r = i * ROWS_PER + lane / CPR;
+    buffer_load_lds16(rs, dst + i * 1024, r * ROW + k_swz(lane % CPR, r, D == 128) * 16);
+  }
+}
+
+// 128 bytes of a float vector [N] into LDS (rows past N read as zeros); one wave.
+__device__ inline void load_vec32(lds_u8* dst, const float* base, int i0, int N, int lane) {
+  const int a = min(i0, N);
+  const i32x4_t rs = make_rsrc(base + a, (N - a) * 4);
+  buffer_load_lds16(rs, dst, lane * 16);
+}
+
+// A operand of a product over 16 tile rows (K-step `ks` of a 32-row block at row
+// `rb0`) taken from the transposed tile: lane j of each 16-lane group reads row
+// 4 half + j/4 (+ 8), columns 32 db + 16 g16 + 4 (j % 4): MFMA row 32 db + l32, and the
+// 16 tile rows in the order of the accumulator rows of a D-layout operand.
+template <int D>
+struct TrOffsets {
+  int lo[D / 32], hi[D / 32];
+  __device__ TrOffsets(int lane) {
+    const int half = lane >> 5, j = lane & 15, g16 = (lane >> 4) & 1;
+    const int rl = 4 * half + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * g16 + ((j & 3) >> 1);
+      lo[db] = SwzTile<D>::at(rl, c) + 8 * (j & 1);
+      hi[db] = SwzTile<D>::at(rl + 8, c) + 8 * (j & 1);
+    }
+  }
+};
+
+// Rows 16 ks .. 16 ks + 15 of a tile differ from rows 0..15 by a multiple of 16, which
+// leaves the k_swz pattern unchanged (it depends on r mod 16, or on (r >> 1) mod 8).
+template <int D>
+__device__ inline u32x4_t tr_operand(const lds_u8* tile, const TrOffsets<D>& off, int db, int row0) {
+  const lds_u8* a = tile + row0 * SwzTile<D>::ROW;
+  const u32x2_t lo = lds_read_tr16(a + off.lo[db]);
+  const u32x2_t hi = lds_read_tr16(a + off.hi[db]);
+  return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Row operand: lane reads row row0 + l32, chunk 2 s + half (dims 16 s + 8 half .. + 8).
+template <int D>
+__device__ inline u32x4_t row_operand(const lds_u8* tile, int row0, int l32, int half, int s) {
+  return lds_read128(tile + SwzTile<D>::at(row0 + l32, 2 * s + half));
+}
+
+// bf16/fp16 pairs of a D-layout accumulator (16 rows of one column per lane), as the
+// B operands of the two 16-row K-steps of a product over those rows.
+template <bool F16>
+__device__ inline void pack_rows(const f32x16_t& x, u32x4_t out[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[h][i] = Elem<F16>::pack2(x[h * 8 + 2 * i], x[h * 8 + 2 * i + 1]);
+}
+
+__device__ inline float unpack_lo(unsigned w, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffff))
+             : __uint_as_float(w << 16);
+}
+__device__ inline float unpack_hi(unsigned w, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16))
+             : __uint_as_float(w & 0xffff0000u);
+}
+
+__device__ inline void wait_all_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------------
+// dQ and D. Wave w owns queries q0 + 32 w + l32 (one MFMA column per lane).
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams p) {
+  typedef Elem<F16> E;
+  typedef SwzTile<D> T;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int BN = 64;                       // keys per tile
+  constexpr int TILE = BN * T::ROW;            // bytes of a K or V tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int bh = blockIdx.y;
+  const int q0 = blockIdx.x * (32 * BW_WAVES);
+  const int my_q = q0 + 32 * wave + l32;
+  const int offset = p.Nkv - p.Nq;
+  const size_t qbase = (size_t)bh * p.Nq, kbase = (size_t)bh * p.Nkv;
+  const uint8_t* kg = (const uint8_t*)p.k + kbase * T::ROW;
+  const uint8_t* vg = (const uint8_t*)p.v + kbase * T::ROW;
+
+  // Q^T and dO^T fragments (B operands: query column l32, dims 16 s + 8 half .. + 8), O
+  // for D = dO . O; rows past N_q read row N_q - 1 (never stored).
+  const size_t row = qbase + min(my_q, p.Nq - 1);
+  u32x4_t qf[KS], dof[KS];
+  float dsum = 0.f;
+  {
+    const uint8_t* qs = (const uint8_t*)p.q + row * T::ROW + half * 16;
+    const uint8_t* ds = (const uint8_t*)p.dout + row * T::ROW + half * 16;
+    const uint8_t* os = (const uint8_t*)p.o + row * T::ROW + half * 16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = *(const u32x4_t*)(qs + s * 32);
+      dof[s] = *(const u32x4_t*)(ds + s * 32);
+      const u32x4_t ov = *(const u32x4_t*)(os + s * 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dsum += unpack_lo(dof[s][e], F16) * unpack_lo(ov[e], F16) +
+                unpack_hi(dof[s][e], F16) * unpack_hi(ov[e], F16);
+    }
+  }
+  const float dval = sum_halves(dsum);
+  if (half == 0 && my_q < p.Nq) p.delta[qbase + my_q] = dval;
+  // log2-domain LSE; a row with no visible key (LSE = -inf) gets P = 0 via +inf.
+  const float lse_raw = p.lse[row];
+  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * 1.4426950408889634f;
+  const float c = p.scale_log2;
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) kv_end = min(p.Nkv, max(0, q0 + 32 * BW_WAVES + offset));
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int wave_last_key = q0 + 32 * wave + 31 + offset;
+
+  f32x16_t dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+  TrOffsets<D> tro(lane);
+  const int limit = CAUSAL ? min(p.Nkv - 1, my_q + offset) : p.Nkv - 1;
+
+  lds_u8* const kl = (lds_u8*)smem;
+  lds_u8* const vl = (lds_u8*)smem + 2 * TILE;
+  if (ntiles > 0) {
+    load_tile<D, BN>(kl, kg, 0, p.Nkv, wave, lane);
+    load_tile<D, BN>(vl, vg, 0, p.Nkv, wave, lane);
+  }
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j & 1;
+    wait_all_and_barrier();  // tile j is in LDS; every wave is done with tile j - 1
+    if (j + 1 < ntiles) {
+      load_tile<D, BN>(kl + (st ^ 1) * TILE, kg, (j + 1) * BN, p.Nkv, wave, lane);
+      load_tile<D, BN>(vl + (st ^ 1) * TILE, vg, (j + 1) * BN, p.Nkv, wave, lane);
+    }
+    if (CAUSAL && j * BN > wave_last_key) continue;  // no key of the tile is visible
+    const lds_u8* kt = kl + st * TILE;
+    const lds_u8* vt = vl + st * TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T for keys j*64 + 32 kb + (accumulator rows).
+      f32x16_t s_acc, dp_acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        s_acc = E::mfma(row_operand<D>(kt, 32 * kb, l32, half, s), qf[s], s_acc);
+        dp_acc = E::mfma(row_operand<D>(vt, 32 * kb, l32, half, s), dof[s], dp_acc);
+      }
+      // P^T and dS^T; register r is key j*64 + 32 kb + 8 (r/4) + 4 half + r%4.
+      const int room = limit - (j * BN + 32 * kb) - 4 * half;
+      f32x16_t ds_acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vis = (r >> 2) * 8 + (r & 3) <= room;
+        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse2)) : 0.f;
+        ds_acc[r] = pr * (dp_acc[r] - dval);
+      }
+      u32x4_t dsf[2];
+      pack_rows<F16>(ds_acc, dsf);
+      // dQ^T += K^T dS^T over the block's 32 keys.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dqacc[db] = E::mfma(tr_operand<D>(kt, tro, db, 32 * kb + 16 * ks), dsf[ks], dqacc[db]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  if (my_q < p.Nq) {
+    const float sc = p.scale;
+    uint8_t* og = (uint8_t*)p.dq + (qbase + my_q) * T::ROW;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2_t w = {E::pack2(dqacc[db][g * 4 + 0] * sc, dqacc[db][g * 4 + 1] * sc),
+                           E::pack2(dqacc[db][g * 4 + 2] * sc, dqacc[db][g * 4 + 3] * sc)};
+        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dK and dV. Wave w owns keys k0 + 32 w + l32 (one MFMA column per lane).
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdParams p) {
+  typedef Elem<F16> E;
+  typedef SwzTile<D> T;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int BK = 32 * BW_WAVES;            // keys per workgroup
+  constexpr int BQ = 32;                       // queries per streamed tile
+  constexpr int KTILE = BK * T::ROW;
+  constexpr int QTILE = BQ * T::ROW;
+  constexpr int STAGE = 2 * QTILE + 2 * 1024;  // Q, dO, LSE, D
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE + 2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int bh = blockIdx.y;
+  const int k0 = blockIdx.x * BK;
+  const int my_k = k0 + 32 * wave + l32;
+  const int offset = p.Nkv - p.Nq;
+  const size_t qbase = (size_t)bh * p.Nq, kbase = (size_t)bh * p.Nkv;
+  const uint8_t* qg = (const uint8_t*)p.q + qbase * T::ROW;
+  const uint8_t* dg = (const uint8_t*)p.dout + qbase * T::ROW;
+
+  lds_u8* const kl = (lds_u8*)smem;
+  lds_u8* const vl = kl + KTILE;
+  lds_u8* const ring = vl + KTILE;
+
+  // Queries that see some key of the workgroup: i >= k0 - offset (causal).
+  int qt0 = 0;
+  if (CAUSAL) qt0 = max(0, k0 - offset) / BQ;
+  const int qt1 = (p.Nq + BQ - 1) / BQ;
+  auto issue = [&](int qt, int st) {
+    lds_u8* s = ring + st * STAGE;
+    load_tile<D, BQ>(s, qg, qt * BQ, p.Nq, wave, lane);
+    load_tile<D, BQ>(s + QTILE, dg, qt * BQ, p.Nq, wave, lane);
+    if (wave == 0) {
+      load_vec32(s + 2 * QTILE, p.lse + qbase, qt * BQ, p.Nq, lane);
+      load_vec32(s + 2 * QTILE + 1024, p.delta + qbase, qt * BQ, p.Nq, lane);
+    }
+  };
+  load_tile<D, BK>(kl, (const uint8_t*)p.k + kbase * T::ROW, k0, p.Nkv, wave, lane);
+  load_tile<D, BK>(vl, (const uint8_t*)p.v + kbase * T::ROW, k0, p.Nkv, wave, lane);
+  if (qt0 < qt1) issue(qt0, 0);
+
+  f32x16_t dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.f;
+  TrOffsets<D> tro(lane);
+  const float c = p.scale_log2;
+  const int wk0 = k0 + 32 * wave;  // this wave's first key
+  const bool key_ok = my_k < p.Nkv;
+
+  for (int qt = qt0; qt < qt1; ++qt) {
+    const int st = (qt - qt0) & 1;
+    wait_all_and_barrier();
+    if (qt + 1 < qt1) issue(qt + 1, st ^ 1);
+    const int qa = qt * BQ;
+    // Causal: the whole tile is past this wave's keys' diagonal when its last query
+    // sees none of them (query i sees key j iff j <= i + offset).
+    if (CAUSAL && qa + BQ - 1 + offset < wk0) continue;
+    const lds_u8* s = ring + st * STAGE;
+    const lds_u8* qtile = s;
+    const lds_u8* dtile = s + QTILE;
+    typedef const __attribute__((address_space(3))) float lds_f32;
+    typedef const __attribute__((address_space(3))) f32x4_t lds_f32x4;
+    lds_f32* lse_t = (lds_f32*)(s + 2 * QTILE);
+    lds_f32* del_t = (lds_f32*)(s + 2 * QTILE + 1024);
+
+    // S = Q K^T and dP = dO V^T: rows = the tile's 32 queries, column = this lane's key.
+    f32x16_t s_acc, dp_acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
+#pragma unroll
+    for (int sk = 0; sk < KS; ++sk) {
+      const u32x4_t kb = row_operand<D>(kl, 32 * wave, l32, half, sk);
+      const u32x4_t vb = row_operand<D>(vl, 32 * wave, l32, half, sk);
+      s_acc = E::mfma(row_operand<D>(qtile, 0, l32, half, sk), kb, s_acc);
+      dp_acc = E::mfma(row_operand<D>(dtile, 0, l32, half, sk), vb, dp_acc);
+    }
+    // Register r is query qa + 8 (r/4) + 4 half + r%4: 4 consecutive queries per r/4.
+    f32x16_t p_acc, ds_acc;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qi = 8 * g + 4 * half;
+      const f32x4_t lz = *(lds_f32x4*)(lse_t + qi);
+      const f32x4_t dz = *(lds_f32x4*)(del_t + qi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const int q = qa + qi + i;
+        // Visible: the key exists, the query exists and (causal) j <= i + offset.
+        const bool vis = key_ok && q < p.Nq && (!CAUSAL || my_k <= q + offset) && lz[i] != -INFINITY;
+        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lz[i] * 1.4426950408889634f)) : 0.f;
+        p_acc[r] = pr;
+        ds_acc[r] = pr * (dp_acc[r] - dz[i]);
+      }
+    }
+    u32x4_t pf[2], dsf[2];
+    pack_rows<F16>(p_acc, pf);
+    pack_rows<F16>(ds_acc, dsf);
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dvacc[db] = E::mfma(tr_operand<D>(dtile, tro, db, 16 * ks), pf[ks], dvacc[db]);
+        dkacc[db] = E::mfma(tr_operand<D>(qtile, tro, db, 16 * ks), dsf[ks], dkacc[db]);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  if (key_ok) {
+    const float sc = p.scale;
+    uint8_t* kgo = (uint8_t*)p.dk + (kbase + my_k) * T::ROW;
+    uint8_t* vgo = (uint8_t*)p.dv + (kbase + my_k) * T::ROW;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = (db * 32 + g * 8 + half * 4) * 2;
+        const u32x2_t wk = {E::pack2(dkacc[db][g * 4 + 0] * sc, dkacc[db][g * 4 + 1] * sc),
+                            E::pack2(dkacc[db][g * 4 + 2] * sc, dkacc[db][g * 4 + 3] * sc)};
+        const u32x2_t wv = {E::pack2(dvacc[db][g * 4 + 0], dvacc[db][g * 4 + 1]),
+                            E::pack2(dvacc[db][g * 4 + 2], dvacc[db][g * 4 + 3])};
+        *(u32x2_t*)(kgo + off) = wk;
+        *(u32x2_t*)(vgo + off) = wv;
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  const int bh = p.B * p.H;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, F16>),
+                     dim3((p.Nq + 32 * BW_WAVES - 1) / (32 * BW_WAVES), bh), dim3(BW_THREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, F16>),
+                     dim3((p.Nkv + 32 * BW_WAVES - 1) / (32 * BW_WAVES), bh), dim3(BW_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool fp16, hipStream_t s) {
+  if (causal) return fp16 ? launch_bwd<D, true, true>(p, s) : launch_bwd<D, true, false>(p, s);
+  return fp16 ? launch_bwd<D, false, true>(p, s) : launch_bwd<D, false, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd16(const BwdParams& p, int d, bool causal, bool fp16, hipStream_t stream) {
+  if (d == 64) return launch_bwd_d<64>(p, causal, fp16, stream);
+  if (d == 128) return launch_bwd_d<128>(p, causal, fp16, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace exattn

@@ -282,6 +282,40 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q,
+             int N_kv, int d_qk, int d_v, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  if (int rc = check_shape(B, H, N_q, N_kv, d_qk, d_v)) return rc;
+  if (d_qk != d_v || (d_qk != 64 && d_qk != 128)) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (int rc = check_scale(scale)) return rc;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_ERR_ALIGN;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  exattn::BwdParams p = {};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = B;
+  p.H = H;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = exattn::launch_bwd16(p, d_qk, causal != 0, dtype == ATTN_FP16,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";

@@ -41,12 +41,30 @@ struct DecodeParams {
   int chunk;            // keys per range, a multiple of 32; splits * chunk >= N_kv
 };
 
+// Arguments of one attention backward (16-bit, dense BHND, d_qk = d_v).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;        // forward output
+  const void* dout;     // gradient of the loss with respect to O
+  const float* lse;     // forward LSE [B, H, N_q]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;         // [B, H, N_q]: D = rowsum(dO * O), written by the first kernel
+  int B, H, Nq, Nkv;
+  float scale;
+  float scale_log2;     // scale * log2(e)
+};
+
 // Launchers (one per instantiation family); return hipError_t of the launch.
 hipError_t launch_fwd16(const FwdParams& p, int d_qk, int d_v, bool causal, bool fp16,
                         int tau, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, bool causal, hipStream_t stream);
 hipError_t launch_decode16(const DecodeParams& p, int d, bool causal, bool fp16,
                            hipStream_t stream);
+hipError_t launch_bwd16(const BwdParams& p, int d, bool causal, bool fp16, hipStream_t stream);
 // Decode workgroups the current device runs at once for head dim d (0 if unknown).
 int decode_resident_workgroups(int d);
 hipError_t launch_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B, int H,

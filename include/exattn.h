@@ -210,6 +210,27 @@ int attn_decode_splits(int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int 
  */
 size_t attn_decode_workspace_bytes(int B, int H, int N_q, int d_v, int splits);
 
+/*
+ * attn_bwd - gradients of attn_fwd: dQ, dK, dV from Q, K, V, the forward's O and
+ * LSE, and dO ("FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for
+ * Asymmetric Hardware Scaling", Figure 2: the scores are recomputed from Q, K and
+ * the saved LSE, then five matrix products and two elementwise steps:
+ * dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q,
+ * with D_i = sum_c dO_ic O_ic).
+ *
+ *   q, k, v, o, dout, dq, dk, dv   dense [B, H, N, d], dtype; o and lse as attn_fwd
+ *                                  wrote them for the same q, k, v, scale, causal
+ *   lse    [B, H, N_q] float32 (rows with LSE = -inf get zero gradients)
+ *   delta  [B, H, N_q] float32 workspace: D is written there (caller-owned)
+ *   d_qk = d_v = 64 or 128, else ATTN_ERR_HEADDIM.
+ *   dq, dk, dv are fully written (rounded to nearest even); the result is
+ *   deterministic (no atomics): one kernel computes D and dQ, a second dK and dV.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             int B, int H, int N_q, int N_kv, int d_qk, int d_v,
+             float scale, int causal, int dtype, void* stream);
+
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* attn_strerror(int code);
 

@@ -40,7 +40,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert names == ["attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd",
+    assert names == ["attn_bwd", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd",
                      "attn_fwd_decode", "attn_fwd_fp8", "attn_fwd_strided", "attn_fwd_tau",
                      "attn_quantize_fp8", "attn_strerror"]
     for n in names:
@@ -159,6 +159,30 @@ def test_attn_fwd_strided_validation(lib):
     assert strided(lib, qs=[32768, 8192, 132]) == c["ATTN_ERR_ALIGN"]     # 264-byte rows
     assert strided(lib, os_=[32772, 8192, 128]) == c["ATTN_ERR_ALIGN"]
     assert strided(lib, causal=3) == c["ATTN_ERR_ARG"]
+
+
+def test_attn_bwd_validation(lib):
+    c = codes()
+    base = [P] * 10 + [1, 2, 64, 64, 128, 128, 0.1, 0, 0, None]
+    f = lib.attn_bwd
+    for i in range(10):
+        a = list(base)
+        a[i] = None
+        assert f(*a) == c["ATTN_ERR_NULL"]
+    a = list(base); a[12] = 0
+    assert f(*a) == c["ATTN_ERR_SHAPE"]
+    a = list(base); a[14], a[15] = 192, 128
+    assert f(*a) == c["ATTN_ERR_HEADDIM"]
+    a = list(base); a[18] = 4
+    assert f(*a) == c["ATTN_ERR_DTYPE"]
+    a = list(base); a[16] = float("nan")
+    assert f(*a) == c["ATTN_ERR_SCALE"]
+    for i in range(10):
+        a = list(base)
+        a[i] = P + 4
+        assert f(*a) == c["ATTN_ERR_ALIGN"]
+    a = list(base); a[17] = 2
+    assert f(*a) == c["ATTN_ERR_ARG"]
 
 
 def dec(lib, **kw):
