@@ -34,8 +34,8 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "device.h",
-                            "tile_io.h", "fp8_ops.h", "mfma16.h", "launch.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "attn_bwd.hip",
+                            "device.h", "tile_io.h", "fp8_ops.h", "mfma16.h", "launch.h")]
 HBM_PEAK = 8000.0  # MI355X HBM3E, GB/s
 
 
@@ -220,6 +220,119 @@ def run_decode(args):
     print(json.dumps(line))
 
 
+def cpu_baseline_bwd(ws, max_heads: int, min_seconds: float = 10.0):
+    """Time the gradient oracle on up to max_heads heads of each workload (TFLOP/s of the
+    five products' algorithmic flops)."""
+    import torch
+
+    import oracle
+    from exact_attention_81_amd import synth
+
+    data = []
+    for w in ws:
+        q, k, v = synth.qkv_for(w)
+        g = torch.Generator("cpu").manual_seed(w.seed + 1)
+        do = torch.randn((w.B, w.H, w.N_q, w.d_v), generator=g).to(torch.bfloat16)
+        f = [oracle.to_f64(x) for x in (q, k, v, do)]
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+        data.append((w, f, heads))
+    flops = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for w, (q, k, v, do), heads in data:
+            for b, h in heads:
+                oracle.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+            flops += 2.5 * w.flops() * len(heads) / (w.B * w.H)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    parts = [f"{len(heads)} of {w.B * w.H} heads of {w.label()}" for w, _, heads in data]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "; ".join(parts) + f", {reps} time(s) ({dt:.1f} s wall, float64 numpy, "
+                                        f"one process)"}
+
+
+def run_bwd(args):
+    """Backward of the default workload: one attn_bwd call per variant per step, the
+    forward (for O and LSE) run once outside the timed region."""
+    from exact_attention_81_amd import synth
+
+    ws = [synth.workload("single", causal=c) for c in (False, True)]
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(ws, min(args.cpu_heads, 16))
+
+    import torch
+
+    import exact_attention_81_amd as ea
+
+    dev = torch.device("cuda:0")
+    calls = []
+    for w in ws:
+        q, k, v = (x.to(dev) for x in synth.qkv_for(w))
+        g = torch.Generator("cpu").manual_seed(w.seed + 1)
+        do = torch.randn((w.B, w.H, w.N_q, w.d_v), generator=g).to(torch.bfloat16).to(dev)
+        o, lse = ea.attn_fwd(q, k, v, causal=w.causal)
+        calls.append((w, lambda q=q, k=k, v=v, o=o, lse=lse, do=do, w=w:
+                      ea.attn_bwd(q, k, v, o, lse, do, causal=w.causal)))
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in calls] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(args.steps):
+        for i, (_, c) in enumerate(calls):
+            evs[s][i][0].record()
+            c()
+            evs[s][i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    bwd_flops = [2.5 * w.flops() for w in ws]  # five products of 2*N_q*N_kv*d per head
+    value = sum(bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    per = []
+    for i, (w, _) in enumerate(calls):
+        durs = sorted(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps))
+        avg = sum(durs) / len(durs)
+        per.append({"variant": "bwd " + w.label(), "avg_launch_us": avg * 1e3,
+                    "tflops": bwd_flops[i] / (avg * 1e-3) / 1e12,
+                    "median_launch_us": 0.5 * (durs[(len(durs) - 1) // 2] + durs[len(durs) // 2]) * 1e3,
+                    "min_launch_us": durs[0] * 1e3})
+    dom = max(range(len(per)), key=lambda i: per[i]["avg_launch_us"])
+    achieved = per[dom]["tflops"]
+    line = {
+        "metric": "attention bwd TFLOP/s (10BHN^2d: five products, causal halved)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: Q,K,V,dO ~ N(0,1) rounded to bf16, seeded torch CPU generator",
+        "config": {"workload": " + ".join("bwd " + w.label() for w in ws), "B": ws[0].B,
+                   "H": ws[0].H, "N_q": ws[0].N_q, "N_kv": ws[0].N_kv, "d": ws[0].d_qk,
+                   "causal": [w.causal for w in ws],
+                   "step": "one attn_bwd call (dQ kernel, then dK/dV kernel) per variant"},
+        "roofline": {"bound": "mfma", "kernel": f"attn_bwd_dq_kernel + attn_bwd_dkdv_kernel "
+                                                f"({per[dom]['variant']})",
+                     "achieved": round(achieved, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK["bf16"], 4), "traffic": committed_traffic("bwd")},
+        "per_variant": per,
+        "kernel_source_sha": kernel_source_hash(),
+        "wall_s_timed_region": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,7 +340,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="single",
                     choices=["single", "tiny", "asym", "fp8", "sweep512", "sweep1024",
-                             "sweep2048", "sweep4096", "sweep8192", "sweep16384", "decode"])
+                             "sweep2048", "sweep4096", "sweep8192", "sweep16384", "decode",
+                             "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--cold-runs", type=int, default=5,
@@ -245,6 +359,9 @@ def main():
 
     if args.workload == "decode":
         run_decode(args)
+        return
+    if args.workload == "bwd":
+        run_bwd(args)
         return
 
     from exact_attention_81_amd import synth

@@ -34,6 +34,7 @@ KERNEL_RE = re.compile(
 FP8_RE = re.compile(r"attn_fwd_fp8_kernel<(true|false)>")
 DEC_RE = re.compile(r"attn_decode_kernel<(\d+), (true|false), (true|false), (\d+)>")
 MERGE_RE = re.compile(r"merge_splits_kernel<(\d+), (true|false)>")
+BWD_RE = re.compile(r"attn_bwd_(dq|dkdv)_kernel<(\d+), (true|false), (true|false)>")
 
 
 def _one(pattern_dir: str, suffix: str) -> str:
@@ -58,6 +59,11 @@ def short_name(name: str) -> str:
         d, causal, f16, nrb = m.groups()
         return (f"attn_decode_kernel d{d} {'causal' if causal == 'true' else 'noncausal'} "
                 f"{'fp16' if f16 == 'true' else 'bf16'} rowblocks{nrb}")
+    m = BWD_RE.search(name)
+    if m:
+        which, d, causal, f16 = m.groups()
+        return (f"attn_bwd_{which}_kernel d{d} {'causal' if causal == 'true' else 'noncausal'} "
+                f"{'fp16' if f16 == 'true' else 'bf16'}")
     m = MERGE_RE.search(name)
     if m:
         return f"merge_splits_kernel d{m.group(1)} {'fp16' if m.group(2) == 'true' else 'bf16'}"
@@ -101,6 +107,8 @@ def algorithmic_bytes(w) -> int:
 
 
 def workloads_of(name: str):
+    if name == "bwd":
+        return [synth.workload("single", causal=c) for c in (False, True)]
     if name == "decode":
         return [synth.decode_workload()]
     if name.startswith("sweep"):
@@ -119,6 +127,20 @@ def variant_key(w) -> str:
     if w.fp8:
         return f"attn_fwd_fp8_kernel d128x128 {mask} e4m3"
     return f"attn_fwd_kernel d{w.d_qk}x{w.d_v} {mask} tau8 bf16"
+
+
+def bwd_keys(w):
+    """Both backward kernels of one call (their counters are summed)."""
+    mask = "causal" if w.causal else "noncausal"
+    return [f"attn_bwd_{k}_kernel d{w.d_qk} {mask} bf16" for k in ("dq", "dkdv")]
+
+
+def bwd_algorithmic_bytes(w) -> int:
+    """Backward: Q, K, V, O, dO read once and LSE; dQ, dK, dV and D written once."""
+    bh = w.B * w.H
+    reads = 2 * (3 * w.N_q * w.d_qk + 2 * w.N_kv * w.d_qk) + 4 * w.N_q
+    writes = 2 * (w.N_q * w.d_qk + 2 * w.N_kv * w.d_qk) + 4 * w.N_q
+    return bh * (reads + writes)
 
 
 def main():
@@ -168,16 +190,20 @@ def main():
               f"and KiB x {f_write * 1024:.1f} (write).", "",
               "| variant | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (scaled) | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|"]
+    bwd = args.workload == "bwd"
     for w in ws:
-        key = variant_key(w)
-        if key not in fetch or key not in write:
+        keys = bwd_keys(w) if bwd else [variant_key(w)]
+        if any(k not in fetch or k not in write for k in keys):
             continue
-        fb = fetch[key][0] * 1024.0 * f_fetch
-        wb = write[key][0] * 1024.0 * f_write
-        alg = algorithmic_bytes(w)
-        traffic[w.label()] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb,
-                              "algorithmic_bytes": alg}
-        lines.append(f"| {w.label()} | {fetch[key][0]:.0f} | {write[key][0]:.0f} | {fb + wb:.4g} | "
+        fk = sum(fetch[k][0] for k in keys)
+        wk = sum(write[k][0] for k in keys)
+        fb = fk * 1024.0 * f_fetch
+        wb = wk * 1024.0 * f_write
+        alg = bwd_algorithmic_bytes(w) if bwd else algorithmic_bytes(w)
+        label = ("bwd " if bwd else "") + w.label()
+        traffic[label] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes": fb + wb,
+                          "algorithmic_bytes": alg}
+        lines.append(f"| {label} | {fk:.0f} | {wk:.0f} | {fb + wb:.4g} | "
                      f"{alg:.4g} | {(fb + wb) / alg:.3f} |")
     lines.append("")
     os.makedirs(args.out, exist_ok=True)
