@@ -28,16 +28,27 @@ namespace {
 constexpr int BW_WAVES = 4;
 constexpr int BW_THREADS = 64 * BW_WAVES;
 
-// Row-major tile of R rows x D 16-bit values in LDS, 16-byte chunks XOR-swizzled by
-// k_swz. Reads: a row piece (A or B operand of a product over D), or, through the
-// transposing read, a block of the transposed tile (A operand of a product over the
-// tile's rows, rows in the order of the MFMA accumulator rows).
+// Chunk position of 16-byte chunk c of row r in tiles that are read both ways: by rows
+// (16 lanes read one chunk of 16 consecutive rows) and transposed (32 lanes read 8 bytes
+// in each of 4 chunks of 4 consecutive rows). The XOR mask takes the 16 rows to 16
+// distinct chunk positions and the 4 x 4 (row, chunk) pairs of a transposed read to 16
+// distinct positions, so neither read meets a bank conflict:
+//   16-chunk rows: mask = 4 (r mod 4) + (r / 4 mod 4);
+//    8-chunk rows (two rows per 256 bytes): mask = 4 (r/2 mod 2) + (r / 4 mod 4).
+__device__ constexpr int b_swz(int c, int r, bool w16) {
+  return w16 ? (c ^ (((r & 3) << 2) | ((r >> 2) & 3))) : (c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)));
+}
+
+// Row-major tile of R rows x D 16-bit values in LDS, 16-byte chunks swizzled by b_swz.
+// Reads: a row piece (A or B operand of a product over D), or, through the transposing
+// read, a block of the transposed tile (A operand of a product over the tile's rows,
+// rows in the order of the MFMA accumulator rows).
 template <int D>
 struct SwzTile {
   static constexpr int ROW = D * 2;
   static constexpr bool W16 = D == 128;
   // Byte offset of chunk c (16 bytes) of row r.
-  static __device__ int at(int r, int c) { return r * ROW + k_swz(c, r, W16) * 16; }
+  static __device__ int at(int r, int c) { return r * ROW + b_swz(c, r, W16) * 16; }
 };
 
 // Direct-to-LDS load of rows [row0, row0 + R) of a [N, D] 16-bit matrix at `base`
@@ -54,7 +65,7 @@ __device__ inline void load_tile(lds_u8* dst, const uint8_t* base, int row0, int
   for (int t = 0; t < NI / BW_WAVES; ++t) {
     const int i = wave + t * BW_WAVES;
     const int r = i * ROWS_PER + lane / CPR;
-    buffer_load_lds16(rs, dst + i * 1024, r * ROW + k_swz(lane % CPR, r, D == 128) * 16);
+    buffer_load_lds16(rs, dst + i * 1024, r * ROW + b_swz(lane % CPR, r, D == 128) * 16);
   }
 }
 
@@ -85,7 +96,7 @@ struct TrOffsets {
 };
 
 // Rows 16 ks .. 16 ks + 15 of a tile differ from rows 0..15 by a multiple of 16, which
-// leaves the k_swz pattern unchanged (it depends on r mod 16, or on (r >> 1) mod 8).
+// leaves the b_swz pattern unchanged (it depends on r mod 16 only).
 template <int D>
 __device__ inline u32x4_t tr_operand(const lds_u8* tile, const TrOffsets<D>& off, int db, int row0) {
   const lds_u8* a = tile + row0 * SwzTile<D>::ROW;
@@ -140,8 +151,11 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int bh = blockIdx.y;
-  const int q0 = blockIdx.x * (32 * BW_WAVES);
+  // One workgroup per (b*H + h, 128-query tile); the tiles of a head on one XCD (they
+  // share its K/V through that XCD's L2), heavy causal tiles first.
+  int bh, qt;
+  map_block(blockIdx.x, (p.Nq + 32 * BW_WAVES - 1) / (32 * BW_WAVES), p.B * p.H, CAUSAL, bh, qt);
+  const int q0 = qt * (32 * BW_WAVES);
   const int my_q = q0 + 32 * wave + l32;
   const int offset = p.Nkv - p.Nq;
   const size_t qbase = (size_t)bh * p.Nq, kbase = (size_t)bh * p.Nkv;
@@ -261,13 +275,19 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
   constexpr int KTILE = BK * T::ROW;
   constexpr int QTILE = BQ * T::ROW;
   constexpr int STAGE = 2 * QTILE + 2 * 1024;  // Q, dO, LSE, D
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE + 2 * STAGE];
+  constexpr int NSTAGE = 3;                    // tile t computed while t+1, t+2 load
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE + NSTAGE * STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int bh = blockIdx.y;
-  const int k0 = blockIdx.x * BK;
+  // One workgroup per (b*H + h, 128-key tile); the tiles of a head on one XCD (they
+  // share its Q, dO through that XCD's L2), causal: the tiles with most queries first.
+  const int nkt = (p.Nkv + BK - 1) / BK;
+  int bh, kt;
+  map_block(blockIdx.x, nkt, p.B * p.H, CAUSAL, bh, kt);
+  if (CAUSAL) kt = nkt - 1 - kt;
+  const int k0 = kt * BK;
   const int my_k = k0 + 32 * wave + l32;
   const int offset = p.Nkv - p.Nq;
   const size_t qbase = (size_t)bh * p.Nq, kbase = (size_t)bh * p.Nkv;
@@ -293,7 +313,11 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
   };
   load_tile<D, BK>(kl, (const uint8_t*)p.k + kbase * T::ROW, k0, p.Nkv, wave, lane);
   load_tile<D, BK>(vl, (const uint8_t*)p.v + kbase * T::ROW, k0, p.Nkv, wave, lane);
-  if (qt0 < qt1) issue(qt0, 0);
+  // Tiles past qt1 are issued too (through empty resources), so every wave has the
+  // same number of loads in flight at each wait: Q and dO pieces, plus LSE and D on
+  // wave 0.
+  issue(qt0, 0);
+  issue(qt0 + 1, 1);
 
   f32x16_t dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -305,10 +329,19 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
   const int wk0 = k0 + 32 * wave;  // this wave's first key
   const bool key_ok = my_k < p.Nkv;
 
+  constexpr int TILE_LOADS = 2 * (QTILE / 1024 / BW_WAVES);
   for (int qt = qt0; qt < qt1; ++qt) {
-    const int st = (qt - qt0) & 1;
-    wait_all_and_barrier();
-    if (qt + 1 < qt1) issue(qt + 1, st ^ 1);
+    const int st = (qt - qt0) % NSTAGE;
+    // Tile qt has landed once at most tile qt+1's loads are outstanding.
+    if (wave == 0) {
+      __builtin_amdgcn_s_waitcnt((TILE_LOADS + 2) | (7 << 4) | (0 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(TILE_LOADS | (7 << 4) | (0 << 8));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(qt + 2, (st + 2) % NSTAGE);
     const int qa = qt * BQ;
     // Causal: the whole tile is past this wave's keys' diagonal when its last query
     // sees none of them (query i sees key j iff j <= i + offset).
@@ -386,11 +419,11 @@ template <int D, bool CAUSAL, bool F16>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int bh = p.B * p.H;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, F16>),
-                     dim3((p.Nq + 32 * BW_WAVES - 1) / (32 * BW_WAVES), bh), dim3(BW_THREADS), 0, s, p);
+                     dim3((p.Nq + 32 * BW_WAVES - 1) / (32 * BW_WAVES) * bh), dim3(BW_THREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, F16>),
-                     dim3((p.Nkv + 32 * BW_WAVES - 1) / (32 * BW_WAVES), bh), dim3(BW_THREADS), 0, s, p);
+                     dim3((p.Nkv + 32 * BW_WAVES - 1) / (32 * BW_WAVES) * bh), dim3(BW_THREADS), 0, s, p);
   return hipGetLastError();
 }
 
