@@ -55,21 +55,21 @@ struct SwzTile {
 // (rows past N read as zeros) into an LDS tile; the waves of the workgroup share the
 // 1 KB instructions: instruction i fills LDS bytes [1024 i, 1024 i + 1024), lane l
 // writes the 16 bytes at 1024 i + 16 l, so it loads the chunk that belongs there.
-template <int D, int R>
+template <int D, int R, int NW = BW_WAVES>
 __device__ inline void load_tile(lds_u8* dst, const uint8_t* base, int row0, int N, int wave, int lane) {
   constexpr int ROW = D * 2, NI = R * ROW / 1024, ROWS_PER = 1024 / ROW, CPR = ROW / 16;
-  static_assert(NI % BW_WAVES == 0, "every wave issues the same number of loads");
+  static_assert(NI % NW == 0, "every wave issues the same number of loads");
   const int r0 = min(row0, N);
   const i32x4_t rs = make_rsrc(base + (size_t)r0 * ROW, (N - r0) * ROW);
 #pragma unroll
-  for (int t = 0; t < NI / BW_WAVES; ++t) {
-    const int i = wave + t * BW_WAVES;
+  for (int t = 0; t < NI / NW; ++t) {
+    const int i = wave + t * NW;
     const int r = i * ROWS_PER + lane / CPR;
     buffer_load_lds16(rs, dst + i * 1024, r * ROW + b_swz(lane % CPR, r, D == 128) * 16);
   }
 }
 
-// 128 bytes of a float vector [N] into LDS (rows past N read as zeros); one wave.
+// 256 floats of a float vector [N] from i0 on into LDS (past N: zeros); one wave.
 __device__ inline void load_vec32(lds_u8* dst, const float* base, int i0, int N, int lane) {
   const int a = min(i0, N);
   const i32x4_t rs = make_rsrc(base + a, (N - a) * 4);
@@ -264,23 +264,29 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams
 }
 
 // ---------------------------------------------------------------------------------
-// dK and dV. Wave w owns keys k0 + 32 w + l32 (one MFMA column per lane).
+// dK and dV. 8 waves: wave w owns keys k0 + 32 (w % 4) + l32 (one MFMA column per lane)
+// and the half w / 4 of each 64-query tile; the two waves of a key block add their
+// partial sums at the end. Two waves per SIMD, so one's products overlap the other's
+// exponentials.
+constexpr int KV_WAVES = 8;
 template <int D, bool CAUSAL, bool F16>
-__global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * KV_WAVES) void attn_bwd_dkdv_kernel(const BwdParams p) {
   typedef Elem<F16> E;
   typedef SwzTile<D> T;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int BK = 32 * BW_WAVES;            // keys per workgroup
-  constexpr int BQ = 32;                       // queries per streamed tile
+  constexpr int BK = 128;                      // keys per workgroup
+  constexpr int BQ = 64;                       // queries per streamed tile
   constexpr int KTILE = BK * T::ROW;
   constexpr int QTILE = BQ * T::ROW;
   constexpr int STAGE = 2 * QTILE + 2 * 1024;  // Q, dO, LSE, D
-  constexpr int NSTAGE = 3;                    // tile t computed while t+1, t+2 load
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE + NSTAGE * STAGE];
+  constexpr int SUM_BYTES = 4 * 2 * DB * 16 * 64 * 4;  // partial dK^T, dV^T of 4 waves
+  constexpr int LDS = 2 * KTILE + 2 * STAGE > SUM_BYTES ? 2 * KTILE + 2 * STAGE : SUM_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, half = lane >> 5;
+  const int kw = wave & 3, qh = wave >> 2;
   // One workgroup per (b*H + h, 128-key tile); the tiles of a head on one XCD (they
   // share its Q, dO through that XCD's L2), causal: the tiles with most queries first.
   const int nkt = (p.Nkv + BK - 1) / BK;
@@ -288,7 +294,8 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
   map_block(blockIdx.x, nkt, p.B * p.H, CAUSAL, bh, kt);
   if (CAUSAL) kt = nkt - 1 - kt;
   const int k0 = kt * BK;
-  const int my_k = k0 + 32 * wave + l32;
+  const int wk0 = k0 + 32 * kw;  // this wave's first key
+  const int my_k = wk0 + l32;
   const int offset = p.Nkv - p.Nq;
   const size_t qbase = (size_t)bh * p.Nq, kbase = (size_t)bh * p.Nkv;
   const uint8_t* qg = (const uint8_t*)p.q + qbase * T::ROW;
@@ -304,20 +311,16 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
   const int qt1 = (p.Nq + BQ - 1) / BQ;
   auto issue = [&](int qt, int st) {
     lds_u8* s = ring + st * STAGE;
-    load_tile<D, BQ>(s, qg, qt * BQ, p.Nq, wave, lane);
-    load_tile<D, BQ>(s + QTILE, dg, qt * BQ, p.Nq, wave, lane);
+    load_tile<D, BQ, KV_WAVES>(s, qg, qt * BQ, p.Nq, wave, lane);
+    load_tile<D, BQ, KV_WAVES>(s + QTILE, dg, qt * BQ, p.Nq, wave, lane);
     if (wave == 0) {
       load_vec32(s + 2 * QTILE, p.lse + qbase, qt * BQ, p.Nq, lane);
       load_vec32(s + 2 * QTILE + 1024, p.delta + qbase, qt * BQ, p.Nq, lane);
     }
   };
-  load_tile<D, BK>(kl, (const uint8_t*)p.k + kbase * T::ROW, k0, p.Nkv, wave, lane);
-  load_tile<D, BK>(vl, (const uint8_t*)p.v + kbase * T::ROW, k0, p.Nkv, wave, lane);
-  // Tiles past qt1 are issued too (through empty resources), so every wave has the
-  // same number of loads in flight at each wait: Q and dO pieces, plus LSE and D on
-  // wave 0.
-  issue(qt0, 0);
-  issue(qt0 + 1, 1);
+  load_tile<D, BK, KV_WAVES>(kl, (const uint8_t*)p.k + kbase * T::ROW, k0, p.Nkv, wave, lane);
+  load_tile<D, BK, KV_WAVES>(vl, (const uint8_t*)p.v + kbase * T::ROW, k0, p.Nkv, wave, lane);
+  if (qt0 < qt1) issue(qt0, 0);
 
   f32x16_t dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -326,44 +329,33 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
     for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.f;
   TrOffsets<D> tro(lane);
   const float c = p.scale_log2;
-  const int wk0 = k0 + 32 * wave;  // this wave's first key
   const bool key_ok = my_k < p.Nkv;
 
-  constexpr int TILE_LOADS = 2 * (QTILE / 1024 / BW_WAVES);
   for (int qt = qt0; qt < qt1; ++qt) {
-    const int st = (qt - qt0) % NSTAGE;
-    // Tile qt has landed once at most tile qt+1's loads are outstanding.
-    if (wave == 0) {
-      __builtin_amdgcn_s_waitcnt((TILE_LOADS + 2) | (7 << 4) | (0 << 8));
-    } else {
-      __builtin_amdgcn_s_waitcnt(TILE_LOADS | (7 << 4) | (0 << 8));
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(qt + 2, (st + 2) % NSTAGE);
-    const int qa = qt * BQ;
-    // Causal: the whole tile is past this wave's keys' diagonal when its last query
-    // sees none of them (query i sees key j iff j <= i + offset).
-    if (CAUSAL && qa + BQ - 1 + offset < wk0) continue;
+    const int st = (qt - qt0) & 1;
+    wait_all_and_barrier();  // tile qt is in LDS; every wave is done with tile qt - 1
+    if (qt + 1 < qt1) issue(qt + 1, st ^ 1);
+    const int qa = qt * BQ + 32 * qh;  // this wave's 32 queries
+    // Causal: none of this wave's queries sees any of its keys (i sees j iff j <= i + offset).
+    if (CAUSAL && qa + 31 + offset < wk0) continue;
     const lds_u8* s = ring + st * STAGE;
     const lds_u8* qtile = s;
     const lds_u8* dtile = s + QTILE;
     typedef const __attribute__((address_space(3))) float lds_f32;
     typedef const __attribute__((address_space(3))) f32x4_t lds_f32x4;
-    lds_f32* lse_t = (lds_f32*)(s + 2 * QTILE);
-    lds_f32* del_t = (lds_f32*)(s + 2 * QTILE + 1024);
+    lds_f32* lse_t = (lds_f32*)(s + 2 * QTILE) + 32 * qh;
+    lds_f32* del_t = (lds_f32*)(s + 2 * QTILE + 1024) + 32 * qh;
 
-    // S = Q K^T and dP = dO V^T: rows = the tile's 32 queries, column = this lane's key.
+    // S = Q K^T and dP = dO V^T: rows = the wave's 32 queries, column = this lane's key.
     f32x16_t s_acc, dp_acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
 #pragma unroll
     for (int sk = 0; sk < KS; ++sk) {
-      const u32x4_t kb = row_operand<D>(kl, 32 * wave, l32, half, sk);
-      const u32x4_t vb = row_operand<D>(vl, 32 * wave, l32, half, sk);
-      s_acc = E::mfma(row_operand<D>(qtile, 0, l32, half, sk), kb, s_acc);
-      dp_acc = E::mfma(row_operand<D>(dtile, 0, l32, half, sk), vb, dp_acc);
+      const u32x4_t kb = row_operand<D>(kl, 32 * kw, l32, half, sk);
+      const u32x4_t vb = row_operand<D>(vl, 32 * kw, l32, half, sk);
+      s_acc = E::mfma(row_operand<D>(qtile, 32 * qh, l32, half, sk), kb, s_acc);
+      dp_acc = E::mfma(row_operand<D>(dtile, 32 * qh, l32, half, sk), vb, dp_acc);
     }
     // Register r is query qa + 8 (r/4) + 4 half + r%4: 4 consecutive queries per r/4.
     f32x16_t p_acc, ds_acc;
@@ -386,22 +378,39 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
     u32x4_t pf[2], dsf[2];
     pack_rows<F16>(p_acc, pf);
     pack_rows<F16>(ds_acc, dsf);
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.
+    // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dvacc[db] = E::mfma(tr_operand<D>(dtile, tro, db, 16 * ks), pf[ks], dvacc[db]);
-        dkacc[db] = E::mfma(tr_operand<D>(qtile, tro, db, 16 * ks), dsf[ks], dkacc[db]);
+        dvacc[db] = E::mfma(tr_operand<D>(dtile, tro, db, 32 * qh + 16 * ks), pf[ks], dvacc[db]);
+        dkacc[db] = E::mfma(tr_operand<D>(qtile, tro, db, 32 * qh + 16 * ks), dsf[ks], dkacc[db]);
       }
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  if (key_ok) {
+  // The two waves of a key block add their partial sums through LDS.
+  wait_all_and_barrier();  // every wave is done with the tiles
+  float* const sums = (float*)smem + kw * (2 * DB * 16 * 64);
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sums[((2 * db) * 16 + r) * 64 + lane] = dkacc[db][r];
+        sums[((2 * db + 1) * 16 + r) * 64 + lane] = dvacc[db][r];
+      }
+  }
+  wait_all_and_barrier();
+  if (qh == 0 && key_ok) {
     const float sc = p.scale;
     uint8_t* kgo = (uint8_t*)p.dk + (kbase + my_k) * T::ROW;
     uint8_t* vgo = (uint8_t*)p.dv + (kbase + my_k) * T::ROW;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[db][r] += sums[((2 * db) * 16 + r) * 64 + lane];
+        dvacc[db][r] += sums[((2 * db + 1) * 16 + r) * 64 + lane];
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int off = (db * 32 + g * 8 + half * 4) * 2;
@@ -412,6 +421,7 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dkdv_kernel(const BwdPara
         *(u32x2_t*)(kgo + off) = wk;
         *(u32x2_t*)(vgo + off) = wv;
       }
+    }
   }
 }
 
@@ -423,7 +433,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, F16>),
-                     dim3((p.Nkv + 32 * BW_WAVES - 1) / (32 * BW_WAVES) * bh), dim3(BW_THREADS), 0, s, p);
+                     dim3((p.Nkv + 127) / 128 * bh), dim3(64 * KV_WAVES), 0, s, p);
   return hipGetLastError();
 }
 
