@@ -49,7 +49,8 @@ def kernel_source_hash() -> str:
 
 def committed_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed counter summary."""
-    path = os.path.join(PROFILES, f"attn_fwd_{workload}_traffic.json")
+    from exact_attention_81_amd.profile_report import profile_stem
+    path = os.path.join(PROFILES, f"{profile_stem(workload)}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:

@@ -12,9 +12,10 @@ The copy kernel of those runs moves a known number of bytes; dividing that by wh
 the counter reads for it gives the factor that turns the counter into bytes. The
 attention kernel's counter times that factor is its HBM traffic per launch.
 
-Writes ``profiles/attn_fwd_<workload>.md`` (figures and the commands that made
-them) and ``profiles/attn_fwd_<workload>_traffic.json`` (read by bench.py, which
-uses it only while the kernel sources hash to the recorded value).
+Writes ``profiles/<stem>.md`` (figures and the commands that made them) and
+``profiles/<stem>_traffic.json`` (read by bench.py, which uses it only while the
+kernel sources hash to the recorded value); ``profile_stem`` names the kernel and
+the workload.
 """
 from __future__ import annotations
 
@@ -143,6 +144,12 @@ def bwd_algorithmic_bytes(w) -> int:
     return bh * (reads + writes)
 
 
+def profile_stem(workload: str) -> str:
+    """File stem of a workload's summary: the kernel it profiles, then the workload."""
+    return {"decode": "attn_decode_splitkv", "bwd": "attn_bwd_single"}.get(workload,
+                                                                       f"attn_fwd_{workload}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -170,7 +177,8 @@ def main():
     ws = workloads_of(args.workload)
     ev = {p["variant"]: p for p in bench["per_variant"]}
     traffic = {}
-    lines = [f"# attn_fwd, workload {args.workload}", "",
+    stem = profile_stem(args.workload)
+    lines = [f"# {stem} (bench.py --workload {args.workload})", "",
              "Workload: " + " + ".join(w.label() for w in ws) + ".", "",
              "## Commands", "", "```", commands, "```", "",
              "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
@@ -207,7 +215,7 @@ def main():
                      f"{alg:.4g} | {(fb + wb) / alg:.3f} |")
     lines.append("")
     os.makedirs(args.out, exist_ok=True)
-    with open(os.path.join(args.out, f"attn_fwd_{args.workload}.md"), "w") as fh:
+    with open(os.path.join(args.out, f"{stem}.md"), "w") as fh:
         fh.write("\n".join(lines))
     dom = bench["roofline"]["kernel"]
     dom_variant = dom[dom.index("(") + 1:-1]
@@ -215,7 +223,7 @@ def main():
            "dominant_variant": dom_variant,
            "hbm_bytes_per_launch": traffic.get(dom_variant, {}).get("hbm_bytes"),
            "per_variant": traffic, "copy_factor_fetch": f_fetch, "copy_factor_write": f_write}
-    with open(os.path.join(args.out, f"attn_fwd_{args.workload}_traffic.json"), "w") as fh:
+    with open(os.path.join(args.out, f"{stem}_traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
 
