@@ -296,15 +296,43 @@ void attn_fwd_kernel(const FwdParams p) {
         for (int r = 0; r < 16; ++r)
           if (!visible(kb, r)) sacc[kb][r] = -INFINITY;
     }
-    float mx = sacc[0][0];
+    // Exponentials against the current reference into pf (rounded to 16 bits); returns
+    // the lane's float32 sum of them.
+    auto exps = [&](float nm) {
+      float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_halves(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const bool grow = mt > m_ref + (float)TAU;
-    if (__any(grow)) {  // wave-uniform branch; only rows past the threshold re-base
+        for (int r = 0; r < 16; ++r) {
+          float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, nm));
+          if constexpr (MASK) e = visible(kb, r) ? e : 0.f;
+          pv[r] = e;
+          ps += e;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = E::pack2(pv[h * 8 + 2 * i], pv[h * 8 + 2 * i + 1]);
+          pf[kb * 2 + h] = w;
+        }
+      }
+      return ps;
+    };
+    // Row max and the rescale of the running state when it grew by more than TAU
+    // doublings; true when any row of the wave re-based (wave-uniform).
+    auto rebase = [&]() {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = max_halves(mx);
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+      const bool grow = mt > m_ref + (float)TAU;
+      if (!__any(grow)) return false;
+      // only rows past the threshold re-base
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
       m_ref = grow ? mt : m_ref;
       l_part *= alpha;
@@ -312,26 +340,24 @@ void attn_fwd_kernel(const FwdParams p) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    const float nm = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, nm));
-        if constexpr (MASK) e = visible(kb, r) ? e : 0.f;
-        pv[r] = e;
-        psum += e;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4_t w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = E::pack2(pv[h * 8 + 2 * i], pv[h * 8 + 2 * i + 1]);
-        pf[kb * 2 + h] = w;
-      }
+      return true;
+    };
+    auto neg_ref = [&]() { return m_ref == -INFINITY ? 0.f : -m_ref; };
+    float psum;
+    if constexpr (DQK > 128) {
+      // d_qk = 192 has no registers to keep S past its exponentials: max first.
+      rebase();
+      psum = exps(neg_ref());
+    } else {
+      // The row max decides the rescale: the reference moves when a score exceeds it
+      // by more than TAU doublings, i.e. when some p = 2^(c s - m_ref) exceeds 2^TAU. A
+      // lane whose p sum to less than 2^TAU has no such p (a float sum of non-negative
+      // terms is at least each term), so the max is needed only where the sum reaches
+      // 2^TAU or no reference exists yet; the decisions, and so the results, are those
+      // of the max test.
+      psum = exps(neg_ref());
+      if (__any(!(psum < (float)(1 << TAU)) || m_ref == -INFINITY))
+        if (rebase()) psum = exps(neg_ref());
     }
     l_part += psum;
   };
