@@ -109,6 +109,15 @@ MANY_ITEM_CASES = [
     (4, 64, 512, 512, 64, 64, True),        # 512 items, two rounds
     (2, 64, 1024, 1024, 128, 128, False),   # 512 items
     (1, 128, 1024, 1024, 128, 128, True),   # 512 items, four query tiles per head
+    # A workgroup that runs several tiles loads the next tile's first K/V tiles during
+    # the current tile's last two iterations: ragged query tiles, N_q > N_kv, key counts
+    # just over one and two key tiles, every head dim.
+    (2, 80, 300, 300, 128, 128, True),      # 320 items, ragged last query tile
+    (2, 80, 300, 200, 128, 128, True),      # N_q > N_kv, first query tile sees 156 keys
+    (4, 72, 256, 100, 128, 128, False),     # 288 items of two key tiles each
+    (3, 88, 256, 130, 64, 64, False),       # three key tiles, ragged last one
+    (3, 88, 256, 320, 192, 128, True),      # d_qk 192
+    (5, 64, 512, 512, 128, 128, True),      # 640 items: 2.5 rounds, heavy/light pairs
 ]
 
 

@@ -30,7 +30,8 @@ def padded(t, dev, pad=8):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 300, 300, 128, 128), (1, 3, 129, 513, 64, 64),
-                                   (2, 2, 257, 255, 192, 128)],
+                                   (2, 2, 257, 255, 192, 128),
+                                   (3, 96, 300, 300, 128, 128)],  # 576 tiles: several per workgroup
                          ids=lambda s: "B{}H{}_{}x{}_d{}x{}".format(*s))
 def test_bnhd_inputs_and_output(shape, causal):
     B, H, nq, nkv, dqk, dv = shape
