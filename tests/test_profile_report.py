@@ -88,3 +88,47 @@ def test_report_end_to_end(tmp_path):
     assert rec["hbm_bytes_per_launch"] == 49500.0 * 1024 * 2 + 33280.0 * 1024
     text = open(f"{out}/attn_fwd_single.md").read()
     assert "python3 bench.py" in text and "| 10 |" in text
+
+
+def test_counter_report_end_to_end(tmp_path):
+    """Derived counter figures: executed flops from MOPS, the clock from the summed
+    GRBM_GUI_ACTIVE of the 8 XCDs, and per-score instruction counts."""
+    from exact_attention_81_amd import counter_report
+    d = str(tmp_path)
+    w = synth.workload("single", causal=False)
+    flops = 2.0 * 4 * 16 * 2048 * 2048 * 256
+    dur_ns = 1.25e5
+    _write(f"{d}/p1/run_kernel_stats.csv",
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+           [[KNAME.format(c="false"), 2, 2 * dur_ns, dur_ns, 100.0, dur_ns, dur_ns, 0.0]])
+    head = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = KNAME.format(c="false")
+    # 2.0 GHz for 125 us = 250000 cycles per XCD, summed over 8
+    _write(f"{d}/p1/run_counter_collection.csv", head,
+           [[k, "MfmaUtil", 50.0], [k, "GRBM_GUI_ACTIVE", 8 * 250000.0], [k, "VALUBusy", 40.0],
+            [k, "LdsUtil", 20.0], [k, "LDSBankConflict", 0.0], [k, "LdsBankConflict", 0.0]])
+    scores = 4 * 16 * 2048 * 2048
+    _write(f"{d}/p2/run_counter_collection.csv", head,
+           [[k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", flops / 512], [k, "SQ_INSTS_VALU_TRANS_F32", scores / 64],
+            [k, "SQ_INSTS_VALU", 5 * scores / 64], [k, "SQ_VALU_MFMA_BUSY_CYCLES", 1000.0],
+            [k, "SQ_VALU_MFMA_COEXEC_CYCLES", 400.0]])
+    with open(f"{d}/commands.txt", "w") as fh:
+        fh.write("rocprofv3 --pmc ...\n")
+    import sys
+    argv = sys.argv
+    sys.argv = ["counter_report", "--workload", "single", "--pmc", f"{d}/p1", f"{d}/p2",
+                "--commands", f"{d}/commands.txt", "--out", f"{d}/out"]
+    try:
+        counter_report.main()
+    finally:
+        sys.argv = argv
+    text = open(f"{d}/out/attn_fwd_single_counters.md").read()
+    rows = {r.split("|")[1].strip(): r.split("|")[2].strip() for r in text.splitlines()
+            if r.startswith("| ") and w.label() in text}
+    assert rows["executed / counted"] == "1.000"
+    assert rows["shader clock"] == "2.000 GHz"
+    assert rows["transcendental instructions per score"] == "1.000"
+    assert rows["VALU instructions per score"] == "5.00"
+    assert rows["MFMA cycles with a co-issued VALU op"] == "40.0 %"
+    rate = flops / (dur_ns * 1e-9) / 1e12
+    assert rows["executed rate / peak at clock"] == format(rate / (2.0 * 256 * 4096 / 1e3) * 100, ".1f") + " %"
