@@ -91,6 +91,35 @@ def cpu_baseline(w_list, max_heads: int, min_seconds: float = 10.0):
                                         f"fork pool)"}
 
 
+def cpu_baseline_one_core(w_list, max_heads: int = 2, min_seconds: float = 3.0):
+    """The oracle in one process with one BLAS thread, on the tiny configuration (every
+    head) and a few heads of each listed workload: the per-core rate beside the pooled
+    baseline."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from exact_attention_81_amd import synth
+
+    out = []
+    with threadpool_limits(1):
+        for w in [synth.workload("tiny")] + list(w_list):
+            q, k, v = synth.qkv_for(w)
+            q, k, v = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+            heads = [(b, h) for b in range(w.B) for h in range(w.H)][:max_heads]
+            done = 0
+            t0 = time.perf_counter()
+            while True:
+                for b, h in heads:
+                    oracle.head(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
+                done += len(heads)
+                dt = time.perf_counter() - t0
+                if dt >= min_seconds / (len(w_list) + 1):
+                    break
+            out.append({"workload": w.label(), "heads": done, "seconds": round(dt, 2),
+                        "value": w.flops() * done / (w.B * w.H) / dt / 1e12, "unit": "TFLOP/s",
+                        "cores": 1, "kind": "oracle"})
+    return out
+
+
 def cpu_baseline_decode(w, max_heads: int, min_seconds: float = 10.0):
     """Time the oracle on up to max_heads query heads of the decode workload (GB/s of the
     call's algorithmic bytes, each query head counted as its share of them)."""
@@ -376,6 +405,8 @@ def main():
         ws = [synth.workload("single", causal=c) for c in (False, True)]
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(ws, args.cpu_heads)
+    # one-core oracle rate on the tiny and single configurations (single workload only)
+    cpu1 = (cpu_baseline_one_core(ws) if cpu is not None and args.workload == "single" else None)
 
     import torch
 
@@ -541,6 +572,8 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }
+    if cpu1 is not None:
+        line["cpu_one_core"] = cpu1
     print(json.dumps(line))
 
 
