@@ -496,24 +496,27 @@ void attn_fwd_kernel(const FwdParams p) {
 
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end
 
-  // ---- Epilogue: O = acc / l, LSE = ln2 * (m + log2 l).
+  // ---- Epilogue: O = acc / l, LSE = ln2 * (m + log2 l). The lane's query and half are
+  // recomputed from the lane id (mbcnt) rather than kept in registers through the loop.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int my_q_e = wq0 + (lane_e & 31), half_e = lane_e >> 5;
   const float l = sum_halves(l_part);
   const bool any = l > 0.f;
   const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
-  if (my_q < p.Nq) {
+  if (my_q_e < p.Nq) {
     uint8_t* __restrict__ og =
-        STRIDED ? (uint8_t*)p.o + (b_ * p.o_sb + h_ * p.o_sh + (long long)my_q * p.o_sn) * 2
-                : (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * DV * 2;
+        STRIDED ? (uint8_t*)p.o + (b_ * p.o_sb + h_ * p.o_sh + (long long)my_q_e * p.o_sn) * 2
+                : (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q_e) * DV * 2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2_t w = {E::pack2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv),
                      E::pack2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv)};
-        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
+        *(u32x2_t*)(og + (db * 32 + g * 8 + half_e * 4) * 2) = w;
       }
-    if (half == 0)
-      p.lse[(size_t)bh * p.Nq + my_q] =
+    if (half_e == 0)
+      p.lse[(size_t)bh * p.Nq + my_q_e] =
           any ? 0.69314718055994531f * (m_ref + __builtin_amdgcn_logf(l)) : -INFINITY;
   }
 }

@@ -390,7 +390,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     for (int i = lane + 64; i < nbk; i += 64) dv_ref = fmaxf(dv_ref, vds[i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dv_ref = fmaxf(dv_ref, __shfl_xor(dv_ref, off));
+    // every lane holds the same maximum: keep it (and its log) in scalar registers
+    dv_ref = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dv_ref)));
     log2_dv_ref = dv_ref > 0.f ? __builtin_amdgcn_logf(dv_ref) : 0.f;
+    log2_dv_ref = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(log2_dv_ref)));
     issue_k(2, 2);
     issue_v(1, 1);
     if (active(0)) s_phase(0);
@@ -413,11 +416,15 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end
 
   // ---- Epilogue: O = dv_ref * acc / l (bf16, RNE), LSE = ln2 * (m_ref - PBIAS + log2 l).
+  // The lane's query and half are recomputed from the lane id (mbcnt) rather than kept
+  // in registers through the loop, where they would be spilled to scratch.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int my_q_e = wq0 + (lane_e & 31), half_e = lane_e >> 5;
   const float l = sum_halves(l_part);
   const bool any = l > 0.f;
   const float inv = any ? dv_ref * __builtin_amdgcn_rcpf(l) : 0.f;
-  if (my_q < p.Nq) {
-    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q) * D * 2;
+  if (my_q_e < p.Nq) {
+    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q_e) * D * 2;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -426,10 +433,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
         const f32x2_t b = {oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv};
         u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
                      __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
-        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
+        *(u32x2_t*)(og + (db * 32 + g * 8 + half_e * 4) * 2) = w;
       }
-    if (half == 0)
-      p.lse[(size_t)bh * p.Nq + my_q] =
+    if (half_e == 0)
+      p.lse[(size_t)bh * p.Nq + my_q_e] =
           any ? 0.69314718055994531f * (m_ref - F8_PBIAS + __builtin_amdgcn_logf(l)) : -INFINITY;
   }
 }

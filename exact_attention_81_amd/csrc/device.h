@@ -64,7 +64,14 @@ __device__ inline float max_halves(float x) {
   return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
-// x + x of lane ^ 32 (used once per kernel, so the LDS-routed shuffle is fine).
-__device__ inline float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+// x + x of lane ^ 32 in every lane of a wave64. After v_permlane32_swap with both
+// operands equal to x, one of r[0], r[1] holds the lane's own x and the other its
+// partner's (which one depends on the lane half), so their sum is the pair's sum,
+// bitwise the same in both halves since float addition commutes. Unlike a shuffle it
+// needs no lane-index register.
+__device__ inline float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace exattn
