@@ -60,7 +60,7 @@ __device__ inline void load_tile(lds_u8* dst, const uint8_t* base, int row0, int
   constexpr int ROW = D * 2, NI = R * ROW / 1024, ROWS_PER = 1024 / ROW, CPR = ROW / 16;
   static_assert(NI % NW == 0, "every wave issues the same number of loads");
   const int r0 = min(row0, N);
-  const i32x4_t rs = make_rsrc(base + (size_t)r0 * ROW, (N - r0) * ROW);
+  const i32x4_t rs = make_rsrc(base + (size_t)r0 * ROW, (unsigned)(N - r0) * ROW);
 #pragma unroll
   for (int t = 0; t < NI / NW; ++t) {
     const int i = wave + t * NW;
@@ -72,7 +72,7 @@ __device__ inline void load_tile(lds_u8* dst, const uint8_t* base, int row0, int
 // 256 floats of a float vector [N] from i0 on into LDS (past N: zeros); one wave.
 __device__ inline void load_vec32(lds_u8* dst, const float* base, int i0, int N, int lane) {
   const int a = min(i0, N);
-  const i32x4_t rs = make_rsrc(base + a, (N - a) * 4);
+  const i32x4_t rs = make_rsrc(base + a, (unsigned)(N - a) * 4u);
   buffer_load_lds16(rs, dst, lane * 16);
 }
 

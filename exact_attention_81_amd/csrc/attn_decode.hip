@@ -117,8 +117,8 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(const DecodePa
   auto key0_of = [&](int u) { return u < my_n ? kv0 + (kp + u * NKP) * DEC_N : p.Nkv; };
   auto issue = [&](int u, int stage) {
     const int key0 = key0_of(u);
-    const i32x4_t krs = make_rsrc(kg + (size_t)key0 * ROW, (p.Nkv - key0) * ROW);
-    const i32x4_t vrs = make_rsrc(vg + (size_t)key0 * ROW, (p.Nkv - key0) * ROW);
+    const i32x4_t krs = make_rsrc(kg + (size_t)key0 * ROW, (unsigned)(p.Nkv - key0) * ROW);
+    const i32x4_t vrs = make_rsrc(vg + (size_t)key0 * ROW, (unsigned)(p.Nkv - key0) * ROW);
     lds_u8* st = ring + stage * STAGE;
 #pragma unroll
     for (int ii = 0; ii < NLD; ++ii) buffer_load_lds16(krs, st + ii * 1024, k_off[ii]);

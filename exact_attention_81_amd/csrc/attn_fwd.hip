@@ -163,7 +163,7 @@ void attn_fwd_kernel(const FwdParams p) {
   // below is a per-lane register plus an immediate offset.
   auto issue_k = [&](int j, auto stage) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * k_row, (p.Nkv - key0) * k_row);
+    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * k_row, (unsigned)(p.Nkv - key0) * (unsigned)k_row);
     lds_u8* st = k_lds + int(stage) * K_STAGE;
 #pragma unroll
     for (int t = 0; t < KA_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, ka_off[t]);
@@ -173,7 +173,7 @@ void attn_fwd_kernel(const FwdParams p) {
   };
   auto issue_v = [&](int j, auto stage) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * v_row, (p.Nkv - key0) * v_row);
+    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * v_row, (unsigned)(p.Nkv - key0) * (unsigned)v_row);
     lds_u8* st = v_lds + int(stage) * V_STAGE;
 #pragma unroll
     for (int t = 0; t < V_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, v_off[t]);
@@ -407,9 +407,9 @@ void attn_fwd_kernel(const FwdParams p) {
   static_assert(ISSUE_GAP >= 1, "one load per PV product at most");
   auto spread_issue = [&](int j, auto k_next, auto v_next) {
     const int kkey0 = min((j + 2) * BLOCK_N, p.Nkv);
-    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * k_row, (p.Nkv - kkey0) * k_row);
+    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * k_row, (unsigned)(p.Nkv - kkey0) * (unsigned)k_row);
     const int vkey0 = min((j + 1) * BLOCK_N, p.Nkv);
-    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * v_row, (p.Nkv - vkey0) * v_row);
+    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * v_row, (unsigned)(p.Nkv - vkey0) * (unsigned)v_row);
     lds_u8* kst = k_lds + int(k_next) * K_STAGE;
     lds_u8* vst = v_lds + int(v_next) * V_STAGE;
     return [=](int step) {

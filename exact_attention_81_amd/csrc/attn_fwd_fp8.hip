@@ -147,10 +147,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     v_off[t] = r * p.Nkv + v_key[t];
   }
   const unsigned v_bytes = (unsigned)(D * p.Nkv);
-  const i32x4_t v_rs = make_rsrc(vg, (int)v_bytes);
+  const i32x4_t v_rs = make_rsrc(vg, v_bytes);
   auto k_rsrc = [&](int j) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    return make_rsrc(kg + (size_t)key0 * D, (p.Nkv - key0) * D);
+    return make_rsrc(kg + (size_t)key0 * D, (unsigned)(p.Nkv - key0) * D);
   };
   // V^T rows continue into the next dim row, so chunks past N_kv (N_kv is a multiple
   // of 16) are pointed past the end of the resource, which reads them as zeros.

@@ -14,10 +14,12 @@ constexpr int kBufferFlags = 0x00020000;
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format.
-__device__ inline i32x4_t make_rsrc(const void* base, int bytes) {
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format. The
+// record count is unsigned: one head's slice of a tensor below 2^31 elements of 2 bytes
+// can span up to 2^32 - 2 bytes.
+__device__ inline i32x4_t make_rsrc(const void* base, unsigned bytes) {
   const unsigned long long a = (unsigned long long)base;
-  return (i32x4_t){(int)(unsigned)a, (int)((a >> 32) & 0xffffu), bytes, kBufferFlags};
+  return (i32x4_t){(int)(unsigned)a, (int)((a >> 32) & 0xffffu), (int)bytes, kBufferFlags};
 }
 
 // 16 bytes per lane from `rsrc` at byte offset `voff` into LDS at dst + 16 * lane

@@ -236,3 +236,47 @@ def test_scale_argument_and_errors():
     bad = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device=dq.device)
     with pytest.raises(ea.AttnError):
         ea.attn_fwd(bad, bad, bad)
+
+
+# ------------------------------------------------------------------ largest accepted K/V slice
+def test_largest_kv_slice_closed_forms():
+    """One head whose K and V each hold just over 2^30 elements at d = 128 (the ABI takes
+    tensors below 2^31 elements), so the byte count of a head's K or V slice passes 2^31
+    (2.15 GB each). The float64 oracle would need 17 GB here, so closed forms decide:
+    * K = 0: every score is 0, O is the mean of V and LSE = ln N_kv (bottom-right causal:
+      row i averages its first i + N_kv - N_q + 1 values);
+    * K's last row = 8 (score 1024 / sqrt(128) against Q = 1, every other score 0): the
+      last key outweighs the other 8.4M by e^-90, so O is its value row (3) and LSE is
+      its score; under the causal mask only the last query row sees it.
+    The split-KV decode path reads the same K and V as one grouped head."""
+    dev = require_gpu()
+    d, n_q = 128, 64
+    n = (1 << 23) + 197  # N_kv * d = 2^30 + 25216 elements; 2^31 + 50432 bytes per tensor
+    log(f"start largest K/V slice N_kv={n} d={d}")
+    q = torch.ones((1, 1, n_q, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device=dev)
+    v = torch.ones((1, 1, n, d), dtype=torch.bfloat16, device=dev)
+    v[0, 0, n - 1] = 2.0 ** 20  # exact in bf16
+    expect_mean = (n - 1 + 2.0 ** 20) / n
+    o, l = run(q, k, v, False)
+    compare(f64(o), f64(l), np.full((1, 1, n_q, d), expect_mean), np.full((1, 1, n_q), np.log(n)),
+            "K = 0, mean of V")
+    od, ld = ea.attn_fwd_decode(q[:, :, :1].expand(1, 8, 1, d).contiguous(), k, v)
+    torch.cuda.synchronize()
+    compare(f64(od), f64(ld), np.full((1, 8, 1, d), expect_mean), np.full((1, 8, 1), np.log(n)),
+            "decode, K = 0, mean of V")
+
+    k[0, 0, n - 1] = 8.0
+    v[0, 0, n - 1] = 3.0
+    s_star = 8.0 * d / np.sqrt(d)
+    lse_star = s_star + np.log1p((n - 1) * np.exp(-s_star))
+    o, l = run(q, k, v, False)
+    compare(f64(o), f64(l), np.full((1, 1, n_q, d), 3.0), np.full((1, 1, n_q), lse_star),
+            "dominant last key")
+    o, l = run(q, k, v, True)
+    seen = np.arange(n_q) + n - n_q + 1  # keys visible to query row i
+    o_ref = np.ones((1, 1, n_q, d))
+    o_ref[0, 0, n_q - 1] = 3.0
+    l_ref = np.log(seen.astype(np.float64))[None, None, :].copy()
+    l_ref[0, 0, n_q - 1] = lse_star
+    compare(f64(o), f64(l), o_ref, l_ref, "dominant last key, causal")
