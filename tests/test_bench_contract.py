@@ -42,3 +42,16 @@ def test_bench_line(workload):
     assert "workload" in line["config"]
     for p in line["per_variant"]:
         assert p["min_launch_us"] <= p["median_launch_us"] and p["cold_avg_launch_us"] > 0
+
+
+def test_one_core_oracle_rate():
+    """The one-core oracle timing runs on the host, one BLAS thread, tiny config first."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from exact_attention_81_amd import synth
+
+    out = bench.cpu_baseline_one_core([synth.workload("tiny")], max_heads=1, min_seconds=0.2)
+    assert [o["workload"] for o in out] == [synth.workload("tiny").label()] * 2
+    for o in out:
+        assert o["cores"] == 1 and o["kind"] == "oracle" and o["unit"] == "TFLOP/s"
+        assert o["value"] > 0 and o["heads"] >= 1
