@@ -24,11 +24,15 @@ constexpr int QTHREADS = 256;
 // values, which float64 holds exactly, so y does not depend on the order of
 // the stages. The first stage (index bit 6) pairs the two halves of the row;
 // each thread reads the whole row and keeps its half of that stage's output,
-// then runs the stages for bits 0-5 on its own 64 values.
+// then runs the stages for bits 0-5 on its own 64 values. Without rotation a
+// thread reads only its half. The column signs are applied as sign-bit flips
+// of the bf16 inputs (negation is exact).
 // Scale: amax = max |y| over the block, ratio = 448 / amax in float64,
 // code = e4m3(float32(y * ratio)) with round-to-nearest-even; the stored
 // descale is float32(amax / div), div = 448 * sqrt(128) (rotated) or 448.
-__global__ __launch_bounds__(QTHREADS) void quantize_kernel(const uint16_t* __restrict__ x,
+// Three waves per SIMD (168 VGPRs, no spills; four would spill the 64 float64 values)
+// keep three workgroups' loads in flight per compute unit.
+__global__ __launch_bounds__(QTHREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void quantize_kernel(const uint16_t* __restrict__ x,
                                                            uint8_t* __restrict__ x8,
                                                            float* __restrict__ descale, int N,
                                                            int nb, const float* __restrict__ signs,
@@ -44,33 +48,47 @@ __global__ __launch_bounds__(QTHREADS) void quantize_kernel(const uint16_t* __re
   const int token = blk * QBLOCK + row;
   const bool valid = token < N;
 
+  // Column signs of the rotation as a 128-bit mask in scalar registers (bit c set:
+  // column c is negated), built by two ballots per wave; zero without rotation.
+  const bool rot = signs != nullptr;
+  unsigned long long neg_lo = 0ull, neg_hi = 0ull;
+  if (rot) {
+    const int lane = tid & 63;
+    neg_lo = __ballot(signs[lane] < 0.f);
+    neg_hi = __ballot(signs[lane + 64] < 0.f);
+  }
+  // XOR pattern that negates the bf16 pair of columns (col, col + 1) of one 32-bit word.
+  auto pair_flip = [](unsigned long long mask, int col) {
+    const unsigned f = (unsigned)(mask >> col) & 3u;
+    return ((f & 1u) << 15) | ((f >> 1) << 31);
+  };
+  auto lo_f = [](unsigned w) { return __uint_as_float(w << 16); };
+  auto hi_f = [](unsigned w) { return __uint_as_float(w & 0xffff0000u); };
+
   double y[64];
   {
     const uint16_t* src = x + ((size_t)bh * N + token) * QD;
-    // Chunk c holds columns 8c..8c+7; chunk c + 8 holds the partner columns + 64.
+    if (rot) {
+      // Chunk c holds columns 8c..8c+7 (a) and the partner columns + 64 (b); the first
+      // stage gives a + b (h = 0) or a - b (h = 1), the latter as a + (-b): negating b
+      // is one more sign-bit flip, folded into b's pattern.
+      const unsigned h_flip = h ? 0x80008000u : 0u;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (valid) {
-        lo = *(const u32x4_t*)(src + c * 8);
-        hi = *(const u32x4_t*)(src + 64 + c * 8);
-      }
+      for (int c = 0; c < 8; ++c) {
+        u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (valid) {
+          lo = *(const u32x4_t*)(src + c * 8);
+          hi = *(const u32x4_t*)(src + 64 + c * 8);
+        }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = c * 8 + e;
-        const unsigned wl = lo[e >> 1], wh = hi[e >> 1];
-        float a = __uint_as_float((e & 1) ? (wl & 0xffff0000u) : (wl << 16));
-        float b = __uint_as_float((e & 1) ? (wh & 0xffff0000u) : (wh << 16));
-        if (signs) {
-          if (signs[col] < 0.f) a = -a;
-          if (signs[col + 64] < 0.f) b = -b;
-          y[col] = h ? (double)a - (double)b : (double)a + (double)b;
-        } else {
-          y[col] = h ? (double)b : (double)a;
+        for (int w = 0; w < 4; ++w) {
+          const int col = c * 8 + 2 * w;
+          const unsigned wl = lo[w] ^ pair_flip(neg_lo, col);
+          const unsigned wh = hi[w] ^ pair_flip(neg_hi, col) ^ h_flip;
+          y[col] = (double)lo_f(wl) + (double)lo_f(wh);
+          y[col + 1] = (double)hi_f(wl) + (double)hi_f(wh);
         }
       }
-    }
-    if (signs) {
 #pragma unroll
       for (int len = 1; len < 64; len <<= 1)
 #pragma unroll
@@ -80,6 +98,18 @@ __global__ __launch_bounds__(QTHREADS) void quantize_kernel(const uint16_t* __re
             y[i] = a + b;
             y[i + len] = a - b;
           }
+    } else {
+      // No rotation: thread h takes columns 64h .. 64h + 63 of its row.
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (valid) v = *(const u32x4_t*)(src + 64 * h + c * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          y[c * 8 + 2 * w] = (double)lo_f(v[w]);
+          y[c * 8 + 2 * w + 1] = (double)hi_f(v[w]);
+        }
+      }
     }
   }
 
