@@ -78,3 +78,34 @@ def test_backward_deterministic_and_empty_rows():
         assert torch.equal(x, y)
     # causal with N_q = 64 > N_kv = 20: queries 0..43 see no key and get dQ = 0
     assert torch.all(a[0][:, :, :44] == 0)
+
+
+def _sampled_heads(B, H, n, d, causal, seed, heads):
+    """Full-size launch; the oracle computes the gradients of a few whole heads."""
+    label = f"bwd B{B} H{H} N{n} d{d} causal={causal} heads {heads}"
+    log("start " + label)
+    q, k, v = synth.qkv(B, H, n, n, d, d, seed)
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    do = torch.randn((B, H, n, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    dq_, dk_, dv_, ddo = to_dev(q, k, v, do)
+    o, lse = ea.attn_fwd(dq_, dk_, dv_, causal=causal)
+    gq, gk, gv = ea.attn_bwd(dq_, dk_, dv_, o, lse, ddo, causal=causal)
+    torch.cuda.synchronize()
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv, _ = oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], d ** -0.5, causal)
+        for name, got, ref in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
+            gate(f64(got[sl]), ref, f"{label} ({b},{h}) {name}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_benchmark_shape(causal):
+    """B4 H16 N2048 d128, the benchmarked backward workload, on two sampled heads."""
+    _sampled_heads(4, 16, 2048, 128, causal, seed=3301 + int(causal), heads=[(0, 0), (3, 15)])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_many_items(causal):
+    """576 workgroups per kernel (more than the 256 compute units), heavy and light
+    causal tiles mixed; every head checked."""
+    run_case(2, 72, 512, 512, 128, causal, seed=3401 + int(causal))
