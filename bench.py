@@ -60,6 +60,23 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def committed_counters(workload: str, variant: str):
+    """Clock, matrix-core busy and related figures of one variant from the committed
+    hardware-counter summary, or None once the kernels have changed since."""
+    from exact_attention_81_amd.profile_report import profile_stem
+    path = os.path.join(PROFILES, f"{profile_stem(workload)}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    fig = rec.get("per_variant", {}).get(variant)
+    if fig is None:
+        return None
+    return dict(fig, source=os.path.relpath(path, ROOT))
+
+
 def cpu_baseline(w_list, max_heads: int, min_seconds: float = 10.0):
     """Time the oracle (as it stands) on up to max_heads heads of each workload.
 
@@ -572,6 +589,9 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }
+    # Hardware-counter figures of the dominant kernel from the committed summary
+    # (rocprofv3 --pmc runs of this workload), null once the kernels have changed.
+    line["counters"] = committed_counters(args.workload, per[dom]["variant"])
     if cpu1 is not None:
         line["cpu_one_core"] = cpu1
     print(json.dumps(line))

@@ -22,13 +22,16 @@ Derived figures (each formula is printed beside it in the summary):
 * LDS: ``LdsUtil``, bank-conflict cycles as a share of GPU time
   (``LDSBankConflict``) and per LDS-active cycle (``LdsBankConflict``).
 
-Writes ``profiles/<stem>_counters.md`` with the commands that made it.
+Writes ``profiles/<stem>_counters.md`` with the commands that made it, and
+``profiles/<stem>_counters.json`` (the headline figures per variant and the kernel
+source hash of the run, read by bench.py).
 """
 from __future__ import annotations
 
 import argparse
 import csv
 import glob
+import json
 import os
 from collections import defaultdict
 
@@ -71,6 +74,8 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--pmc", nargs="+", required=True)
     ap.add_argument("--commands", required=True)
+    ap.add_argument("--bench-json", default=None,
+                    help="bench.py's output of the first pass (gives the kernel source hash)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
 
@@ -85,6 +90,7 @@ def main():
              "## Commands", "", "```", commands, "```", ""]
 
     bwd = args.workload == "bwd"
+    record = {}  # per variant key: the figures bench.py attaches to its line
     for w in workloads_of(args.workload):
         keys = bwd_keys(w) if bwd else [variant_key(w)]
         for key in keys:
@@ -110,6 +116,15 @@ def main():
             trans_per_score = get("SQ_INSTS_VALU_TRANS_F32") * 64 / sc if get("SQ_INSTS_VALU_TRANS_F32") else None
             coexec = (get("SQ_VALU_MFMA_COEXEC_CYCLES") / get("SQ_VALU_MFMA_BUSY_CYCLES")
                       if get("SQ_VALU_MFMA_COEXEC_CYCLES") and get("SQ_VALU_MFMA_BUSY_CYCLES") else None)
+            r1 = lambda v: None if v is None else round(v, 1)
+            record[w.label() if not bwd else f"{key} ({w.label()})"] = {
+                "clock_ghz": None if clock_ghz is None else round(clock_ghz, 3),
+                "mfma_busy_pct": r1(get("MfmaUtil")),
+                "rate_over_peak_at_clock_pct": (round(rate / peak_at_clock * 100, 1)
+                                                if rate and peak_at_clock else None),
+                "valu_busy_pct": r1(get("VALUBusy")),
+                "lds_bank_conflict_pct": r1(get("LDSBankConflict")),
+                "executed_over_counted": (round(exec_flops / alg, 4) if exec_flops and alg else None)}
             lines += [f"## {key} ({w.label()})", "",
                       "| figure | value | how |", "|---|---|---|",
                       f"| duration | {fmt(dur_us, '.1f')} us | kernel trace of the first pass |",
@@ -142,6 +157,13 @@ def main():
     path = os.path.join(args.out, f"{stem}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
+    sha = None
+    if args.bench_json:
+        with open(args.bench_json) as fh:
+            sha = json.loads(fh.read().strip().splitlines()[-1]).get("kernel_source_sha")
+    with open(os.path.join(args.out, f"{stem}.json"), "w") as fh:
+        json.dump({"workload": args.workload, "kernel_source_sha": sha, "per_variant": record}, fh,
+                  indent=1)
     print(path)
 
 

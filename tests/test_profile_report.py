@@ -132,3 +132,7 @@ def test_counter_report_end_to_end(tmp_path):
     assert rows["MFMA cycles with a co-issued VALU op"] == "40.0 %"
     rate = flops / (dur_ns * 1e-9) / 1e12
     assert rows["executed rate / peak at clock"] == format(rate / (2.0 * 256 * 4096 / 1e3) * 100, ".1f") + " %"
+    rec = json.load(open(f"{d}/out/attn_fwd_single_counters.json"))
+    fig = rec["per_variant"][w.label()]
+    assert rec["kernel_source_sha"] is None  # no bench output given
+    assert fig["clock_ghz"] == 2.0 and fig["mfma_busy_pct"] == 50.0 and fig["executed_over_counted"] == 1.0
