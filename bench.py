@@ -60,6 +60,14 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def device_info(dev):
+    """The GPU the line was measured on: name, architecture, compute units, memory."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "memory_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
 def committed_counters(workload: str, variant: str):
     """Clock, matrix-core busy and related figures of one variant from the committed
     hardware-counter summary, or None once the kernels have changed since."""
@@ -264,6 +272,7 @@ def run_decode(args):
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }
+    line["device"] = device_info(dev)
     print(json.dumps(line))
 
 
@@ -377,6 +386,7 @@ def run_bwd(args):
         "wall_s_timed_region": round(wall, 4),
         "cpu_baseline": cpu,
     }
+    line["device"] = device_info(dev)
     print(json.dumps(line))
 
 
@@ -592,6 +602,7 @@ def main():
     # Hardware-counter figures of the dominant kernel from the committed summary
     # (rocprofv3 --pmc runs of this workload), null once the kernels have changed.
     line["counters"] = committed_counters(args.workload, per[dom]["variant"])
+    line["device"] = device_info(dev)
     if cpu1 is not None:
         line["cpu_one_core"] = cpu1
     print(json.dumps(line))

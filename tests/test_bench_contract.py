@@ -25,7 +25,7 @@ def test_bench_line(workload):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
-    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "device",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
         assert key in line, key
