@@ -55,3 +55,24 @@ def test_one_core_oracle_rate():
     for o in out:
         assert o["cores"] == 1 and o["kind"] == "oracle" and o["unit"] == "TFLOP/s"
         assert o["value"] > 0 and o["heads"] >= 1
+
+
+def test_committed_profiles_follow_kernel_sources(tmp_path, monkeypatch):
+    """Traffic and counter figures are reported only while the kernel sources hash to
+    the value recorded with them."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    variant = "single:B4_H16_Nq2048_Nkv2048_d128x128_noncausal_bf16"
+    (tmp_path / "attn_fwd_single_traffic.json").write_text(json.dumps(
+        {"kernel_source_sha": "abc", "hbm_bytes_per_launch": 123.0}))
+    (tmp_path / "attn_fwd_single_counters.json").write_text(json.dumps(
+        {"kernel_source_sha": "abc", "per_variant": {variant: {"clock_ghz": 1.9}}}))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    assert bench.committed_traffic("single") == 123.0
+    assert bench.committed_counters("single", variant)["clock_ghz"] == 1.9
+    assert bench.committed_counters("single", "other variant") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "def")
+    assert bench.committed_traffic("single") is None
+    assert bench.committed_counters("single", variant) is None
