@@ -102,6 +102,25 @@ def _bf16_block(seed, B=1, H=2, N=300, d=128, outliers=True):
     return x.to(torch.bfloat16)
 
 
+def test_rotation_golden_sign_then_hadamard():
+    """Hand-derived d = 4 example (tests/golden/rotation_sign_hadamard_4.json): the signs
+    act on x's coordinates before the Hadamard mixing, x R = x diag(sigma) H / sqrt(d).
+    R R^T = I and |R_ij| = 1/sqrt(d) hold for H diag(sigma) too; this value does not."""
+    with open(os.path.join(GOLDEN, "rotation_sign_hadamard_4.json")) as fh:
+        g = json.load(fh)
+    x = np.array(g["x"])
+    sigma = np.array(g["sigma"])
+    np.testing.assert_array_equal(x @ oracle.rotation(sigma), g["x_rotated"])
+    assert not np.allclose(x @ oracle.rotation(sigma), g["x_rotated_other_order"])
+    # the quantiser applies the same rotation (unnormalised) and rounds 336 to even 320
+    xb = torch.tensor(x, dtype=torch.float32).view(1, 1, 1, 4).to(torch.bfloat16)
+    codes, desc = oracle.quantize_blocks(xb, sigma)
+    np.testing.assert_array_equal(oracle.e4m3_decode(codes).reshape(-1), g["quantised_values"])
+    assert desc.reshape(-1)[0] == np.float32(g["descale"])
+    np.testing.assert_allclose(oracle.dequantize_blocks(codes, desc).reshape(-1),
+                               np.array(g["quantised_values"]) * np.float32(g["descale"]))
+
+
 @pytest.mark.parametrize("rotate", [False, True])
 def test_block_quantisation_bounds(rotate):
     x = _bf16_block(1)
