@@ -23,7 +23,14 @@
 // where dv is the tile's V descale and dv_ref the largest V descale of the
 // head: the ratio folds V's dequantisation into the exponent (no per-tile
 // rescale of the accumulator), and O = dv_ref * acc / l at the end. The row
-// sum l adds p / (dv / dv_ref), i.e. the unrounded 2^(s - m_ref + PBIAS).
+// sum l adds the e4m3-rounded p, the very weights the PV product uses, divided
+// by dv / dv_ref: the final weights p / l then sum to one exactly. With three
+// mantissa bits, summing the unrounded p instead would leave every row off by
+// the rounding of its largest weights (up to 2^-4), which on rows dominated by
+// a few keys moves O by that share of |v|. The sum comes from the matrix core:
+// one more e4m3 product per 64 keys, an all-ones A operand against the same
+// P^T operand, gives every lane its query's sum over the 64 keys (the vector
+// ALU, the busier unit here, is spared one add per score).
 // The running maximum m_ref is re-based when the row maximum grows by more
 // than TAU doublings (section 3.2 of the first page), so every p is at most
 // 2^(TAU + PBIAS) = 256, inside e4m3's range (448), while a row's largest
@@ -148,15 +155,17 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   }
   const unsigned v_bytes = (unsigned)(D * p.Nkv);
   const i32x4_t v_rs = make_rsrc(vg, v_bytes);
+  // Tiles j >= ntiles (past N_kv, or past the causal diagonal of the query tile) go
+  // through an empty resource or past its end: they read zeros and touch no memory.
   auto k_rsrc = [&](int j) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    return make_rsrc(kg + (size_t)key0 * D, (unsigned)(p.Nkv - key0) * D);
+    return make_rsrc(kg + (size_t)key0 * D, j < ntiles ? (unsigned)(p.Nkv - key0) * D : 0u);
   };
   // V^T rows continue into the next dim row, so chunks past N_kv (N_kv is a multiple
   // of 16) are pointed past the end of the resource, which reads them as zeros.
   auto v_voff = [&](int j, int t) {
     const int key0 = j * BLOCK_N;
-    return (key0 + v_key[t] < p.Nkv) ? v_off[t] + key0 : (int)v_bytes;
+    return (j < ntiles && key0 + v_key[t] < p.Nkv) ? v_off[t] + key0 : (int)v_bytes;
   };
   auto issue_k = [&](int j, auto stage) {
     const i32x4_t rs = k_rsrc(j);
@@ -193,7 +202,8 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   f32x16_t sacc[NKB];
   i32x8_t pf[NKC];           // P^T B operands (e4m3) between softmax and PV
   float m_ref = -INFINITY;   // running reference max, log2 units (bias excluded)
-  float l_part = 0.f;
+  float l_row = 0.f;         // the query's row sum (the same in both lane halves)
+  float tile_inv_ratio = 1.f;  // dv_ref / dv of the tile between its softmax and PV
 
   // S(j): S^T = K_j Q^T. Operands are read one product ahead of their MFMA.
   auto s_phase = [&](auto stage) {
@@ -218,6 +228,8 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   };
 
   // PV(j): O^T += V_j^T P_j^T, operands two products ahead; hook(step) issues tile loads.
+  // The row sum of the rounded P comes from two more products, ones^T P^T (every A
+  // byte 1.0 in e4m3, 0x38), issued with the first PV products and read at the end.
   auto pv_phase = [&](auto stage, auto hook) {
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
     constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
@@ -226,14 +238,22 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
       return join8(lds_read128(st + voff[kc][0] + db * 32 * VT_ROW), lds_read128(st + voff[kc][1] + db * 32 * VT_ROW));
     };
     i32x8_t vf[2] = {vread(0), vread(1)};
+    const int one = 0x38383838;
+    const i32x8_t ones = {one, one, one, one, one, one, one, one};
+    f32x16_t lsum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum[r] = 0.f;
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
       const i32x8_t cur = vf[step % 2];
       if (step + 2 < STEPS) vf[step % 2] = vread(step + 2);
       oacc[step % 4] = mfma_f8(cur, pf[step / 4], oacc[step % 4]);
+      if (step < NKC) lsum = mfma_f8(ones, pf[step], lsum);
       hook(step);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // every row of the ones product holds the query's sum over the tile's keys
+    l_row = fmaf(lsum[0], tile_inv_ratio, l_row);
   };
   auto no_hook = [](int) {};
 
@@ -246,7 +266,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     const float dv = vds[blk];
     // log2(dv / dv_ref) <= 0; a zero block (all codes 0) keeps the bias 0.
     const float vbias = dv > 0.f ? __builtin_amdgcn_logf(dv) - log2_dv_ref : 0.f;
-    const float inv_ratio = __builtin_amdgcn_exp2f(-vbias);
+    tile_inv_ratio = __builtin_amdgcn_exp2f(-vbias);
     int room = 0;
     auto visible = [&](int kb, int r) { return kb * 32 + (r >> 2) * 8 + (r & 3) <= room; };
     if constexpr (MASK) {
@@ -269,24 +289,19 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     if (__any(grow)) {
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
       m_ref = grow ? mt : m_ref;
-      l_part *= alpha;
+      l_row *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
     const float nm = ((m_ref == -INFINITY) ? 0.f : -m_ref) + F8_PBIAS + vbias;
-    float psum = 0.f;
     unsigned w[NKB][4];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float pv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], ct, nm));
-        pv[r] = e;
-        psum += e;
-      }
+      for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], ct, nm));
 #pragma unroll
       for (int q = 0; q < 4; ++q) w[kb][q] = pack4_fp8(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
     }
@@ -300,7 +315,6 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
         pf[kc][2 * q] = (int)r[0];
         pf[kc][2 * q + 1] = (int)r[1];
       }
-    l_part += psum * inv_ratio;
   };
 
   int j_plain = min(ntiles, p.Nkv / BLOCK_N);
@@ -385,8 +399,12 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     // first use, and since it does not see the tile loads it waits for every load
     // (vmcnt(0)). Using them here, before K(2) and V(1) are issued, keeps that wait
     // from covering those two.
+    // A negative scale is applied here as -Q (sign bits only, exact) with |scale| in c.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) asm volatile("" : "+v"(qf[ks]));
+    for (int ks = 0; ks < 2; ++ks) {
+      asm volatile("" : "+v"(qf[ks]));
+      qf[ks] ^= (int)p.q_neg;
+    }
     for (int i = lane + 64; i < nbk; i += 64) dv_ref = fmaxf(dv_ref, vds[i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dv_ref = fmaxf(dv_ref, __shfl_xor(dv_ref, off));
@@ -420,7 +438,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   // in registers through the loop, where they would be spilled to scratch.
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int my_q_e = wq0 + (lane_e & 31), half_e = lane_e >> 5;
-  const float l = sum_halves(l_part);
+  const float l = l_row;
   const bool any = l > 0.f;
   const float inv = any ? dv_ref * __builtin_amdgcn_rcpf(l) : 0.f;
   if (my_q_e < p.Nq) {
