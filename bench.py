@@ -1,13 +1,15 @@
 """Benchmark of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload target]
 
 A step is one pass of the hot path over one batch of synthetic input that is
-already resident in HBM. For the default workload (B=4, H=16, N=2048, d=128,
-bfloat16) a step is one non-causal and one causal attn_fwd call. The line
-printed is the whole-job throughput in TFLOP/s, counting 4*B*H*N^2*d flops per
-non-causal call (2*B*H*N_q*N_kv*(d_qk+d_v) in general) and half that for a
-causal one.
+already resident in HBM. The default workload is the 16384-token sequence sweep
+(H=16, d=128, bfloat16, B=16384/N) at the lengths the throughput target is set
+for, N = 4096, 8192 and 16384: a step is one non-causal and one causal attn_fwd
+call at each N (six calls). The line printed is the whole-job throughput in
+TFLOP/s, counting 4*B*H*N^2*d flops per non-causal call (2*B*H*N_q*N_kv*(d_qk+d_v)
+in general) and half that for a causal one, with the rate and share of the peak
+of every call beside it.
 
 Alongside it:
   * roofline: the dominant kernel's algorithmic flops per launch divided by its
@@ -34,8 +36,10 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_81_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "attn_bwd.hip",
-                            "device.h", "tile_io.h", "fp8_ops.h", "mfma16.h", "launch.h")]
+                  for f in ("attn_fwd.hip", "attn_fwd_fp8.hip", "attn_fp8.hip", "attn_decode.hip",
+                            "attn_bwd.hip", "exattn_api.cpp", "device.h", "tile_io.h", "fp8_ops.h",
+                            "mfma16.h", "launch.h")]
+TARGET_N = (4096, 8192, 16384)  # sequence lengths of the throughput target
 HBM_PEAK = 8000.0  # MI355X HBM3E, GB/s
 
 
@@ -58,6 +62,19 @@ def committed_traffic(workload: str):
     if rec.get("kernel_source_sha") != kernel_source_hash():
         return None  # the kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's description."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def device_info(dev):
@@ -112,8 +129,9 @@ def cpu_baseline(w_list, max_heads: int, min_seconds: float = 10.0):
             break
     parts = [f"{len(heads)} of {w.B * w.H} heads of {w.label()}" for w, _, heads in data]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": procs, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "; ".join(parts) + f", {reps} time(s) ({dt:.1f} s wall, float64 numpy, "
-                                        f"fork pool)"}
+                                        f"fork pool of {procs} processes, one BLAS thread each)"}
 
 
 def cpu_baseline_one_core(w_list, max_heads: int = 2, min_seconds: float = 3.0):
@@ -166,6 +184,7 @@ def cpu_baseline_decode(w, max_heads: int, min_seconds: float = 10.0):
         if dt >= min_seconds:
             break
     return {"value": per_head * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{len(heads)} of {w.B * w.H} query heads of {w.label()}, "
                       f"{done // len(heads)} time(s) ({dt:.1f} s wall, float64 numpy, one process)"}
 
@@ -306,6 +325,7 @@ def cpu_baseline_bwd(ws, max_heads: int, min_seconds: float = 10.0):
             break
     parts = [f"{len(heads)} of {w.B * w.H} heads of {w.label()}" for w, _, heads in data]
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "; ".join(parts) + f", {reps} time(s) ({dt:.1f} s wall, float64 numpy, "
                                         f"one process)"}
 
@@ -395,12 +415,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="single",
-                    choices=["single", "tiny", "asym", "fp8", "sweep512", "sweep1024",
+    ap.add_argument("--workload", default="target",
+                    choices=["target", "single", "tiny", "asym", "fp8", "sweep512", "sweep1024",
                              "sweep2048", "sweep4096", "sweep8192", "sweep16384", "decode",
                              "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="heads of each variant the CPU oracle is timed on (default: 16 for "
+                         "the target workload, 64 otherwise)")
     ap.add_argument("--cold-runs", type=int, default=5,
                     help="launches per variant timed after evicting the caches (0: none)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -414,6 +436,8 @@ def main():
               f"run this same one-GPU workload.", file=sys.stderr)
         sys.exit(2)
 
+    if args.cpu_heads is None:
+        args.cpu_heads = 16 if args.workload == "target" else 64
     if args.workload == "decode":
         run_decode(args)
         return
@@ -423,7 +447,9 @@ def main():
 
     from exact_attention_81_amd import synth
 
-    if args.workload.startswith("sweep"):
+    if args.workload == "target":
+        ws = [synth.workload("sweep", causal=c, N=n) for n in TARGET_N for c in (False, True)]
+    elif args.workload.startswith("sweep"):
         n = int(args.workload[5:])
         ws = [synth.workload("sweep", causal=c, N=n) for c in (False, True)]
     elif args.workload in ("tiny", "asym", "fp8"):
@@ -577,9 +603,14 @@ def main():
                  if fp8 else "synthetic: Q,K,V ~ N(0,1) rounded to bf16, seeded torch CPU generator"),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "config": {
-            "workload": " + ".join(w.label() for w in ws),
-            "B": w0.B, "H": w0.H, "N_q": w0.N_q, "N_kv": w0.N_kv, "d_qk": w0.d_qk,
-            "d_v": w0.d_v, "causal": [w.causal for w in ws],
+            "workload": ("sequence sweep of 16384 tokens (B = 16384/N, H 16, d 128, bf16) at "
+                         f"N = {', '.join(str(n) for n in TARGET_N)}, non-causal and causal: "
+                         if args.workload == "target" else "") + " + ".join(w.label() for w in ws),
+            "B": [w.B for w in ws] if len({w.B for w in ws}) > 1 else w0.B,
+            "H": w0.H,
+            "N_q": [w.N_q for w in ws] if len({w.N_q for w in ws}) > 1 else w0.N_q,
+            "N_kv": [w.N_kv for w in ws] if len({w.N_kv for w in ws}) > 1 else w0.N_kv,
+            "d_qk": w0.d_qk, "d_v": w0.d_v, "causal": [w.causal for w in ws],
             "step": ("one attn_fwd_fp8 call on prepared e4m3 inputs" if fp8
                      else "one attn_fwd call per listed variant"),
         },

@@ -83,9 +83,11 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _check(t, name, dtypes):
+def _check(t, name, dtypes, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
@@ -98,9 +100,35 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check_strided(t, name, dtypes):
+def _check_output(t, name, shape, dtype, device, dense=True):
+    """A caller-supplied output: the kernels write every element of ``shape`` through a
+    raw pointer, so anything smaller, of another dtype or on another device is refused."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_vector(t, name, numel, dtype, device):
+    """A float32 side input read by index (descales): contiguous and at least as long
+    as the kernels index it."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _check_strided(t, name, dtypes, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if t.dim() != 4:
@@ -122,8 +150,8 @@ def _fwd(q, k, v, causal, scale, tau, out, lse):
             raise ValueError("attn_fwd_tau takes contiguous tensors")
         return _fwd_strided(q, k, v, causal, scale, out, lse)
     _check(q, "q", (torch.bfloat16, torch.float16))
-    _check(k, "k", (q.dtype,))
-    _check(v, "v", (q.dtype,))
+    _check(k, "k", (q.dtype,), q.device)
+    _check(v, "v", (q.dtype,), q.device)
     B, H, n_q, d_qk = q.shape
     n_kv, d_v = k.shape[2], v.shape[3]
     if k.shape != (B, H, n_kv, d_qk) or v.shape != (B, H, n_kv, d_v):
@@ -132,8 +160,10 @@ def _fwd(q, k, v, causal, scale, tau, out, lse):
         scale = d_qk ** -0.5
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    _check_output(out, "out", (B, H, n_q, d_v), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    _check_output(lse, "lse", (B, H, n_q), torch.float32, q.device)
     dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
     lib = load_library()
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_kv, d_qk, d_v,
@@ -153,8 +183,8 @@ def _fwd_strided(q, k, v, causal, scale, out, lse):
     import torch
 
     _check_strided(q, "q", (torch.bfloat16, torch.float16))
-    _check_strided(k, "k", (q.dtype,))
-    _check_strided(v, "v", (q.dtype,))
+    _check_strided(k, "k", (q.dtype,), q.device)
+    _check_strided(v, "v", (q.dtype,), q.device)
     B, H, n_q, d_qk = q.shape
     n_kv, d_v = k.shape[2], v.shape[3]
     if k.shape != (B, H, n_kv, d_qk) or v.shape != (B, H, n_kv, d_v):
@@ -164,8 +194,10 @@ def _fwd_strided(q, k, v, causal, scale, out, lse):
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
     _check_strided(out, "out", (q.dtype,))
+    _check_output(out, "out", (B, H, n_q, d_v), q.dtype, q.device, dense=False)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    _check_output(lse, "lse", (B, H, n_q), torch.float32, q.device)
     dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
     rc = load_library().attn_fwd_strided(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_kv, d_qk, d_v,
@@ -226,15 +258,22 @@ def attn_fwd_fp8(q8, k8, v8t, q_descale, k_descale, v_descale, *, causal: bool =
     d_v = v8t.shape[2]
     if k8.shape != (B, H, n_kv, d_qk) or v8t.shape != (B, H, d_v, n_kv):
         raise ValueError("shape mismatch between q8, k8 and v8t")
-    for name, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
-        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    for name, t in (("k8", k8), ("v8t", v8t)):
+        if t.device != q8.device:
+            raise ValueError(f"{name} must be on {q8.device}")
+    nbq = (n_q + FP8_BLOCK - 1) // FP8_BLOCK
+    nbk = (n_kv + FP8_BLOCK - 1) // FP8_BLOCK
+    for name, t, nb in (("q_descale", q_descale, nbq), ("k_descale", k_descale, nbk),
+                        ("v_descale", v_descale, nbk)):
+        _check_vector(t, name, B * H * nb, torch.float32, q8.device)
     if scale is None:
         scale = d_qk ** -0.5
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=torch.bfloat16, device=q8.device)
+    _check_output(out, "out", (B, H, n_q, d_v), torch.bfloat16, q8.device)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q8.device)
+    _check_output(lse, "lse", (B, H, n_q), torch.float32, q8.device)
     rc = load_library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_descale),
                                      _ptr(k_descale), _ptr(v_descale), _ptr(out), _ptr(lse),
                                      B, H, n_q, n_kv, d_qk, d_v, float(scale), int(bool(causal)),
@@ -263,8 +302,8 @@ def attn_fwd_decode(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     import torch
 
     _check(q, "q", (torch.bfloat16, torch.float16))
-    _check(k, "k", (q.dtype,))
-    _check(v, "v", (q.dtype,))
+    _check(k, "k", (q.dtype,), q.device)
+    _check(v, "v", (q.dtype,), q.device)
     B, H, n_q, d = q.shape
     H_kv, n_kv = k.shape[1], k.shape[2]
     if k.shape != (B, H_kv, n_kv, d) or v.shape != (B, H_kv, n_kv, v.shape[3]):
@@ -279,10 +318,15 @@ def attn_fwd_decode(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     need = lib.attn_decode_workspace_bytes(B, H, n_q, d_v, splits)
     if workspace is None and need:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    if workspace is not None and (not workspace.is_cuda or workspace.device != q.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous GPU tensor on {q.device}")
     if out is None:
         out = torch.empty((B, H, n_q, d_v), dtype=q.dtype, device=q.device)
+    _check_output(out, "out", (B, H, n_q, d_v), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    _check_output(lse, "lse", (B, H, n_q), torch.float32, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
     rc = lib.attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, n_q, n_kv,
@@ -298,9 +342,10 @@ def attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _check(t, name, (torch.bfloat16, torch.float16) if name == "q" else (q.dtype,))
-    if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 GPU tensor")
+        _check(t, name, (torch.bfloat16, torch.float16) if name == "q" else (q.dtype,), q.device)
+    if not lse.is_cuda or lse.device != q.device or lse.dtype != torch.float32 or \
+            not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 GPU tensor on the device of q")
     B, H, n_q, d = q.shape
     n_kv = k.shape[2]
     if k.shape != (B, H, n_kv, d) or v.shape != (B, H, n_kv, d) or o.shape != q.shape or \

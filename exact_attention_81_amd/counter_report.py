@@ -35,21 +35,29 @@ import json
 import os
 from collections import defaultdict
 
-from .profile_report import ROOT, bwd_keys, kernel_stats, profile_stem, short_name, variant_key, workloads_of
+from .profile_report import (ROOT, assign_variants, bwd_keys, kernel_stats, profile_stem, short_name,
+                             trace_per_variant, variant_key, workloads_of)
 
 CUS = 256            # MI355X compute units
 XCDS = 8             # GRBM_GUI_ACTIVE instances summed in the CSV
 MFMA_FLOP_PER_CLK_CU = {"bf16": 4096, "fp8": 8192}
 
 
-def counters(dirs):
-    """{short kernel name: {counter: mean value per dispatch}} over all runs."""
+def counters(dirs, ws=None):
+    """{short kernel name: {counter: mean value per dispatch}} over all runs; with the
+    workload's variants ``ws`` also keyed by variant label (dispatch order)."""
     vals = defaultdict(lambda: defaultdict(list))
     for d in dirs:
         for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
             with open(path) as fh:
-                for r in csv.DictReader(fh):
-                    vals[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                rows = list(csv.DictReader(fh))
+            lab = assign_variants(rows, ws) if ws else {}
+            for r in rows:
+                v = float(r["Counter_Value"])
+                vals[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(v)
+                did = int(r["Dispatch_Id"])
+                if did in lab:
+                    vals[lab[did]][r["Counter_Name"]].append(v)
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
 
 
@@ -80,7 +88,11 @@ def main():
     args = ap.parse_args()
 
     stats = {r["name"]: r for r in kernel_stats(args.pmc[0])}
-    cnt = counters(args.pmc)
+    ws_all = workloads_of(args.workload)
+    fwd = args.workload not in ("bwd", "decode")
+    cnt = counters(args.pmc, ws_all if fwd else None)
+    if fwd:  # per-variant durations from the kernel trace (variants may share a kernel)
+        stats.update({k: v for k, v in trace_per_variant(args.pmc[0], ws_all).items()})
     with open(args.commands) as fh:
         commands = fh.read().strip()
     stem = profile_stem(args.workload) + "_counters"
@@ -91,8 +103,8 @@ def main():
 
     bwd = args.workload == "bwd"
     record = {}  # per variant key: the figures bench.py attaches to its line
-    for w in workloads_of(args.workload):
-        keys = bwd_keys(w) if bwd else [variant_key(w)]
+    for w in ws_all:
+        keys = bwd_keys(w) if bwd else [w.label() if fwd else variant_key(w)]
         for key in keys:
             c = cnt.get(key)
             if c is None:
@@ -125,7 +137,7 @@ def main():
                 "valu_busy_pct": r1(get("VALUBusy")),
                 "lds_bank_conflict_pct": r1(get("LDSBankConflict")),
                 "executed_over_counted": (round(exec_flops / alg, 4) if exec_flops and alg else None)}
-            lines += [f"## {key} ({w.label()})", "",
+            lines += [f"## {variant_key(w) if fwd else key} ({w.label()})", "",
                       "| figure | value | how |", "|---|---|---|",
                       f"| duration | {fmt(dur_us, '.1f')} us | kernel trace of the first pass |",
                       f"| matrix cores busy | {fmt(get('MfmaUtil'), '.1f')} % | MfmaUtil = "

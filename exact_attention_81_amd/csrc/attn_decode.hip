@@ -153,6 +153,13 @@ __global__ __launch_bounds__(DEC_THREADS) void attn_decode_kernel(const DecodePa
 
   issue(0, 0);
   issue(1, 1);
+  // A negative scale is applied as -Q (sign bits only, exact) with |scale| in c. The
+  // empty asm keeps the wait for the Q loads after the first tile loads are issued.
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    asm volatile("" : "+v"(qf[s]));
+    qf[s] ^= p.q_neg;
+  }
   for (int u = 0; u < my_n; ++u) {
     const int stage = u & 1;
     const lds_u8* st = ring + stage * STAGE;

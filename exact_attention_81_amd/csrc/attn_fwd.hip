@@ -156,14 +156,19 @@ void attn_fwd_kernel(const FwdParams p) {
     const int r = i * rows_per + lane / cpr;
     v_off[t] = r * v_row + v_swz(lane % cpr, r, V_W16) * 16;
   }
-  // Tiles past the last one are still "loaded" through an empty resource (every lane
-  // reads zero bytes), which keeps the number of loads in flight the same at every
-  // barrier; the stages they fill are not read again.
+  // Tiles past the last one (j >= ntiles: past N_kv, or past the causal diagonal of
+  // the query tile) are still "loaded" through an empty resource (every lane reads
+  // zero bytes and no memory is touched), which keeps the number of loads in flight
+  // the same at every barrier; the stages they fill are not read again.
   // `stage` is an int or a std::integral_constant; with the latter every LDS address
   // below is a per-lane register plus an immediate offset.
-  auto issue_k = [&](int j, auto stage) {
+  auto tile_rsrc = [&](const uint8_t* g, int j, int row) {
     const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(kg + (size_t)key0 * k_row, (unsigned)(p.Nkv - key0) * (unsigned)k_row);
+    const unsigned bytes = j < ntiles ? (unsigned)(p.Nkv - key0) * (unsigned)row : 0u;
+    return make_rsrc(g + (size_t)key0 * row, bytes);
+  };
+  auto issue_k = [&](int j, auto stage) {
+    const i32x4_t rs = tile_rsrc(kg, j, k_row);
     lds_u8* st = k_lds + int(stage) * K_STAGE;
 #pragma unroll
     for (int t = 0; t < KA_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, ka_off[t]);
@@ -172,8 +177,7 @@ void attn_fwd_kernel(const FwdParams p) {
       buffer_load_lds16(rs, st + KA_BYTES + (wave + t * NWAVES) * 1024, kb_off[t]);
   };
   auto issue_v = [&](int j, auto stage) {
-    const int key0 = min(j * BLOCK_N, p.Nkv);
-    const i32x4_t rs = make_rsrc(vg + (size_t)key0 * v_row, (unsigned)(p.Nkv - key0) * (unsigned)v_row);
+    const i32x4_t rs = tile_rsrc(vg, j, v_row);
     lds_u8* st = v_lds + int(stage) * V_STAGE;
 #pragma unroll
     for (int t = 0; t < V_PER; ++t) buffer_load_lds16(rs, st + (wave + t * NWAVES) * 1024, v_off[t]);
@@ -406,10 +410,8 @@ void attn_fwd_kernel(const FwdParams p) {
   constexpr int ISSUE_GAP = PV_STEPS / LOADS_PER_TILE;
   static_assert(ISSUE_GAP >= 1, "one load per PV product at most");
   auto spread_issue = [&](int j, auto k_next, auto v_next) {
-    const int kkey0 = min((j + 2) * BLOCK_N, p.Nkv);
-    const i32x4_t krs = make_rsrc(kg + (size_t)kkey0 * k_row, (unsigned)(p.Nkv - kkey0) * (unsigned)k_row);
-    const int vkey0 = min((j + 1) * BLOCK_N, p.Nkv);
-    const i32x4_t vrs = make_rsrc(vg + (size_t)vkey0 * v_row, (unsigned)(p.Nkv - vkey0) * (unsigned)v_row);
+    const i32x4_t krs = tile_rsrc(kg, j + 2, k_row);
+    const i32x4_t vrs = tile_rsrc(vg, j + 1, v_row);
     lds_u8* kst = k_lds + int(k_next) * K_STAGE;
     lds_u8* vst = v_lds + int(v_next) * V_STAGE;
     return [=](int step) {
@@ -472,8 +474,12 @@ void attn_fwd_kernel(const FwdParams p) {
     // The compiler waits for the Q fragments at their first use, and since it does not
     // see the tile loads it waits for every load (vmcnt(0)). Touching the fragments
     // here, before K(2) and V(1) are issued, keeps that wait from covering those two.
+    // A negative scale is applied here as -Q (sign bits only, exact) with |scale| in c.
 #pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qf[s]));
+    for (int s = 0; s < KS; ++s) {
+      asm volatile("" : "+v"(qf[s]));
+      qf[s] ^= p.q_neg;
+    }
     issue_k(2, 2);
     issue_v(1, 1);
     if (active(0)) s_phase(0);

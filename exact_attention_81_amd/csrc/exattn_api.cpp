@@ -38,8 +38,17 @@ int check_shape(int B, int H, int N_q, int N_kv, int d_qk, int d_v) {
   return ATTN_OK;
 }
 
-int check_scale(float scale) {
-  return (std::isfinite(scale) && scale >= 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
+int check_scale(float scale) { return std::isfinite(scale) ? ATTN_OK : ATTN_ERR_SCALE; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The forward kernels take the row maximum of Q K^T times a non-negative factor. A
+// negative scale is carried by negating Q instead: scale * (q . k) = |scale| * ((-q) . k),
+// and flipping the sign bit of every Q element in registers is exact. Returns the XOR
+// mask the kernels apply to each 32-bit word of Q (two 16-bit or four 8-bit elements).
+unsigned q_sign_mask(float scale, bool fp8) {
+  if (!std::signbit(scale) || scale == 0.f) return 0u;
+  return fp8 ? 0x80808080u : 0x80008000u;
 }
 
 // Element strides (batch, head, row) of the four 16-bit tensors, in the order q, k, v, o.
@@ -72,6 +81,25 @@ int check_strides_shape(const Strides16& st, int N_q, int N_kv, int d_qk, int d_
   return ATTN_OK;
 }
 
+// O is written by many workgroups at once, so no two of its elements may share an
+// address: with the dimensions of extent > 1 sorted by stride, each stride must reach
+// past every element the smaller ones span (a sufficient condition; a layout that
+// interleaves dimensions in some other non-overlapping way is refused too).
+bool o_overlaps(const int64_t (&st)[3], int B, int H, int N_q, int d_v) {
+  int64_t dims[3][2] = {{st[0], B}, {st[1], H}, {st[2], N_q}};
+  // insertion sort of the three (stride, extent) pairs by stride
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && dims[j][0] < dims[j - 1][0]; --j)
+      for (int c = 0; c < 2; ++c) std::swap(dims[j][c], dims[j - 1][c]);
+  int64_t span = d_v;  // elements of one row (stride 1)
+  for (auto& dm : dims) {
+    if (dm[1] <= 1) continue;
+    if (dm[0] < span) return true;
+    span = dm[0] * (dm[1] - 1) + span;
+  }
+  return false;
+}
+
 // 16-byte loads and stores need every stride to be a multiple of 8 elements.
 bool strides_aligned(const Strides16& st) {
   for (int t = 0; t < 4; ++t)
@@ -88,6 +116,7 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
   const Strides16 st = strided ? *strided : dense_strides(H, N_q, N_kv, d_qk, d_v);
   if (strided) {
     if (int rc = check_strides_shape(st, N_q, N_kv, d_qk, d_v)) return rc;
+    if (o_overlaps(st.v[3], B, H, N_q, d_v)) return ATTN_ERR_SHAPE;
   }
   if (!supported_dims16(d_qk, d_v)) return ATTN_ERR_HEADDIM;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
@@ -111,7 +140,8 @@ int fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int 
   p.H = H;
   p.Nq = N_q;
   p.Nkv = N_kv;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = std::fabs(scale) * kLog2e;
+  p.q_neg = q_sign_mask(scale, false);
   hipError_t e = exattn::launch_fwd16(p, d_qk, d_v, causal != 0, dtype == ATTN_FP16, tau,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -224,7 +254,8 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t, const
   p.H = H;
   p.Nq = N_q;
   p.Nkv = N_kv;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = std::fabs(scale) * kLog2e;
+  p.q_neg = q_sign_mask(scale, true);
   hipError_t e = exattn::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -274,7 +305,8 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   p.Hkv = H_kv;
   p.Nq = N_q;
   p.Nkv = N_kv;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = std::fabs(scale) * kLog2e;
+  p.q_neg = q_sign_mask(scale, false);
   p.splits = splits;
   p.chunk = decode_chunk(N_kv, splits);
   hipError_t e = exattn::launch_decode16(p, d_qk, causal != 0, dtype == ATTN_FP16,
@@ -310,7 +342,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.Nq = N_q;
   p.Nkv = N_kv;
   p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = scale * kLog2e;  // the backward uses the saved LSE, no row maximum
   hipError_t e = exattn::launch_bwd16(p, d_qk, causal != 0, dtype == ATTN_FP16,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -323,7 +355,7 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_SHAPE: return "invalid shape (a size < 1, a tensor with >= 2^31 elements, or N not a multiple of 16 where required)";
     case ATTN_ERR_HEADDIM: return "unsupported head dimensions";
     case ATTN_ERR_DTYPE: return "unsupported dtype";
-    case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+    case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
     case ATTN_ERR_ARG: return "argument out of range";

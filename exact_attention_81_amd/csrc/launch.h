@@ -17,7 +17,8 @@ struct FwdParams {
   const float* k_descale;
   const float* v_descale;
   int B, H, Nq, Nkv;
-  float scale_log2;     // softmax scale * log2(e), >= 0
+  float scale_log2;     // |softmax scale| * log2(e)
+  unsigned q_neg;       // XOR mask for every 32-bit word of Q: the sign bits when scale < 0
   int n_qtiles;         // ceil(N_q / BLOCK_M)
   // 16-bit path: element strides of Q, K, V and O along batch, head and row (the last
   // dim is dense). Row strides times N are below 2^30, so byte offsets of rows fit in
@@ -36,7 +37,8 @@ struct DecodeParams {
   float* o_part;        // splits > 1: [splits, B*H*N_q, d] fp32, O_s normalised by its own sum
   float* lse_part;      // splits > 1: [splits, B*H*N_q] fp32
   int B, H, Hkv, Nq, Nkv;
-  float scale_log2;     // softmax scale * log2(e), >= 0
+  float scale_log2;     // |softmax scale| * log2(e)
+  unsigned q_neg;       // XOR mask for every 32-bit word of Q: the sign bits when scale < 0
   int splits;           // key ranges per (batch, KV head)
   int chunk;            // keys per range, a multiple of 32; splits * chunk >= N_kv
 };
@@ -54,7 +56,7 @@ struct BwdParams {
   void* dv;
   float* delta;         // [B, H, N_q]: D = rowsum(dO * O), written by the first kernel
   int B, H, Nq, Nkv;
-  float scale;
+  float scale;         // any finite value
   float scale_log2;     // scale * log2(e)
 };
 

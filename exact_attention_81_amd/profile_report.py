@@ -75,6 +75,48 @@ def short_name(name: str) -> str:
     return name[:60]
 
 
+def _rows(d: str, suffix: str):
+    with open(_one(d, suffix)) as fh:
+        return list(csv.DictReader(fh))
+
+
+def assign_variants(rows, ws):
+    """{Dispatch_Id: workload label} for the attention dispatches among ``rows``.
+
+    bench.py launches the variants of a workload in one fixed order (warm-up, timed
+    steps and cold runs alike), and variants may share a kernel instance and grid
+    (the target workload's three sequence lengths do), so the k-th dispatch of the
+    listed kernels belongs to variant k mod len(ws). The kernel names must follow
+    that cycle, else the run is not a bench.py run of this workload."""
+    keys = [variant_key(w) for w in ws]
+    name_of = {}
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        if name in keys:
+            name_of[int(r["Dispatch_Id"])] = name
+    out = {}
+    for i, did in enumerate(sorted(name_of)):
+        if name_of[did] != keys[i % len(ws)]:
+            raise ValueError(f"dispatch {did} ({name_of[did]}) breaks the launch order "
+                             f"{keys} of the workload")
+        out[did] = ws[i % len(ws)].label()
+    return out
+
+
+def trace_per_variant(d: str, ws):
+    """Per workload variant: mean, min and max kernel duration (us) and launch count,
+    from the kernel trace of a --kernel-trace run."""
+    rows = _rows(d, "kernel_trace.csv")
+    lab = assign_variants(rows, ws)
+    durs = defaultdict(list)
+    for r in rows:
+        did = int(r["Dispatch_Id"])
+        if did in lab:
+            durs[lab[did]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: {"avg_us": sum(v) / len(v), "min_us": min(v), "max_us": max(v), "calls": len(v)}
+            for k, v in durs.items()}
+
+
 def kernel_stats(d: str):
     rows = []
     with open(_one(d, "kernel_stats.csv")) as fh:
@@ -85,13 +127,19 @@ def kernel_stats(d: str):
     return rows
 
 
-def counter_per_dispatch(d: str, counter: str):
-    """Mean value of one counter per dispatch, by short kernel name."""
+def counter_per_dispatch(d: str, counter: str, ws=None):
+    """Mean value of one counter per dispatch, by short kernel name and, when the
+    workload's variants ``ws`` are given, also by variant label (dispatch order)."""
+    rows = _rows(d, "counter_collection.csv")
+    lab = assign_variants(rows, ws) if ws else {}
     vals = defaultdict(list)
-    with open(_one(d, "counter_collection.csv")) as fh:
-        for r in csv.DictReader(fh):
-            if r["Counter_Name"] == counter:
-                vals[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            v = float(r["Counter_Value"])
+            vals[short_name(r["Kernel_Name"])].append(v)
+            did = int(r["Dispatch_Id"])
+            if did in lab:
+                vals[lab[did]].append(v)
     return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
 
 
@@ -107,7 +155,12 @@ def algorithmic_bytes(w) -> int:
     return bh * (2 * ins + 2 * w.N_q * w.d_v + 4 * w.N_q)
 
 
+TARGET_N = (4096, 8192, 16384)
+
+
 def workloads_of(name: str):
+    if name == "target":
+        return [synth.workload("sweep", causal=c, N=n) for n in TARGET_N for c in (False, True)]
     if name == "bwd":
         return [synth.workload("single", causal=c) for c in (False, True)]
     if name == "decode":
@@ -167,14 +220,16 @@ def main():
     with open(args.commands) as fh:
         commands = fh.read().strip()
     stats = kernel_stats(args.stats)
-    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
-    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    ws = workloads_of(args.workload)
+    fwd = args.workload not in ("bwd", "decode")
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE", ws if fwd else None)
+    write = counter_per_dispatch(args.write, "WRITE_SIZE", ws if fwd else None)
+    per_var = trace_per_variant(args.stats, ws) if fwd else {}
     copy_name = "copy (torch.neg, float32)"
     copy_bytes = args.copy_mib << 20
     f_fetch = copy_bytes / (fetch[copy_name][0] * 1024.0)
     f_write = copy_bytes / (write[copy_name][0] * 1024.0)
 
-    ws = workloads_of(args.workload)
     ev = {p["variant"]: p for p in bench["per_variant"]}
     traffic = {}
     stem = profile_stem(args.workload)
@@ -186,6 +241,15 @@ def main():
     for r in stats:
         lines.append(f"| {r['name']} | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
                      f"{r['max_us']:.2f} | {r['pct']:.2f} |")
+    if per_var:
+        lines += ["", "Per variant, from the same kernel trace (dispatches attributed to the "
+                  "variants in bench.py's launch order):", "",
+                  "| variant | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for w in ws:
+            t = per_var.get(w.label())
+            if t:
+                lines.append(f"| {w.label()} | {t['calls']} | {t['avg_us']:.2f} | "
+                             f"{t['min_us']:.2f} | {t['max_us']:.2f} |")
     lines += ["", "bench.py's HIP-event average of the same launches (the run under --stats):", "",
               "| variant | avg us (events) | TFLOP/s (GB/s for decode) |", "|---|---|---|"]
     for p in bench["per_variant"]:
@@ -200,7 +264,7 @@ def main():
               "|---|---|---|---|---|---|"]
     bwd = args.workload == "bwd"
     for w in ws:
-        keys = bwd_keys(w) if bwd else [variant_key(w)]
+        keys = bwd_keys(w) if bwd else [w.label() if fwd else variant_key(w)]
         if any(k not in fetch or k not in write for k in keys):
             continue
         fk = sum(fetch[k][0] for k in keys)
@@ -222,6 +286,7 @@ def main():
     rec = {"workload": args.workload, "kernel_source_sha": bench["kernel_source_sha"],
            "dominant_variant": dom_variant,
            "hbm_bytes_per_launch": traffic.get(dom_variant, {}).get("hbm_bytes"),
+           "trace_avg_us_per_variant": {k: round(v["avg_us"], 3) for k, v in per_var.items()},
            "per_variant": traffic, "copy_factor_fetch": f_fetch, "copy_factor_write": f_write}
     with open(os.path.join(args.out, f"{stem}_traffic.json"), "w") as fh:
         json.dump(rec, fh, indent=1)

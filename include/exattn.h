@@ -51,7 +51,7 @@ enum {
     ATTN_ERR_HEADDIM = -3, /* (d_qk, d_v) not one of (64,64), (128,128), (192,128);
                               for the fp8 entry points only (128,128) */
     ATTN_ERR_DTYPE = -4,   /* dtype is neither ATTN_BF16 nor ATTN_FP16 */
-    ATTN_ERR_SCALE = -5,   /* scale is negative, NaN or infinite */
+    ATTN_ERR_SCALE = -5,   /* scale is NaN or infinite */
     ATTN_ERR_ALIGN = -6,   /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_HIP = -7,     /* the kernel launch failed (hipGetLastError) */
     ATTN_ERR_ARG = -8      /* another argument is out of range (tau, transpose flag) */
@@ -67,7 +67,10 @@ enum {
  *   lse  [B, H, N_q]         float32  natural-log logsumexp of the scaled scores,
  *                                     ln(sum_j exp(scale * q_i . k_j)) over visible j;
  *                                     fully written
- *   scale   softmax scale, finite and >= 0 (usually 1/sqrt(d_qk))
+ *   scale   softmax scale, any finite value (usually 1/sqrt(d_qk)); a negative
+ *           scale is computed as |scale| applied to -Q (the sign bits of Q are
+ *           flipped in registers, which is exact), so that the row maximum the
+ *           online softmax keeps is that of the scaled scores
  *   causal  0: every key is visible. 1: key j is visible to query i iff
  *           j <= i + (N_kv - N_q) (bottom-right aligned; the lower triangle
  *           when N_q == N_kv). A query with no visible key gets O = 0 and
@@ -95,7 +98,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   Every stride must be >= 0, row strides at least the row length (d_qk for q and
  *   k, d_v for v and o) and row stride * N below 2^30, batch and head strides below
  *   2^40 (else ATTN_ERR_SHAPE); every stride a multiple of 8 elements (16 bytes, else
- *   ATTN_ERR_ALIGN). lse stays dense [B, H, N_q]. o must not overlap q, k, v or lse.
+ *   ATTN_ERR_ALIGN). lse stays dense [B, H, N_q]. o must not overlap q, k, v or lse,
+ *   and no two elements of o may share an address: sorted by stride, each of o's
+ *   batch, head and row strides (over dimensions of extent > 1) must be at least the
+ *   span of the smaller ones, else ATTN_ERR_SHAPE. q, k and v may overlap (e.g. a
+ *   head stride of 0 repeats one K/V head for every query head).
  */
 int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int N_q, int N_kv, int d_qk, int d_v,

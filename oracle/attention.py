@@ -153,7 +153,7 @@ def attention_parallel(q, k, v, scale: float, causal: bool = False,
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, H = q.shape[:2]
     todo = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    processes = processes or os.cpu_count() or 1
+    processes = processes or min(16, os.cpu_count() or 1)
     ctx = mp.get_context("fork")
     with ctx.Pool(processes, initializer=_worker_init,
                   initargs=(q, k, v, scale, causal)) as pool:

@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: device placement, gates, case logging."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -43,6 +45,15 @@ def f64(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def record(label: str, stats: dict) -> None:
+    """Append one case's error figures as a JSON line to the file named by
+    EXATTN_PARITY_RECORD (nothing when it is unset)."""
+    path = os.environ.get("EXATTN_PARITY_RECORD")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(dict(case=label, **stats)) + "\n")
+
+
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, label: str, atol=O_ATOL, rtol=O_RTOL,
             mean_tol=O_MEAN, lse_tol=LSE_ATOL):
     """Gate GPU outputs (numpy float64) against the oracle; returns the stats."""
@@ -56,8 +67,21 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, label: str, atol=O_ATOL, rtol=O_RTOL
     assert np.array_equal(np.isfinite(lse_gpu), fin), f"{label}: LSE finiteness differs"
     assert np.all(lse_gpu[~fin] == lse_ref[~fin]), f"{label}: empty rows must have LSE -inf"
     stats["lse_max_abs"] = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+    stats["elements"] = int(err.size)
+    # The part of the error no 16-bit output can avoid: the exact result rounded to
+    # bfloat16 (reported when every GPU value is a bfloat16 value).
+    import torch
+
+    og = torch.from_numpy(np.ascontiguousarray(o_gpu))
+    if torch.equal(og.to(torch.bfloat16).double(), og):
+        ideal = np.abs(torch.from_numpy(np.ascontiguousarray(o_ref)).to(torch.bfloat16).double().numpy()
+                       - o_ref)
+        stats["bf16_rounding_max_abs"] = float(ideal.max())
+        stats["max_abs_beyond_rounding"] = float((err - ideal).max())
     log(f"{label}: O max abs {stats['max_abs']:.3e} (vs 1e-2), mean abs {stats['mean_abs']:.3e}, "
-        f"worst err/bound {stats['worst_ratio']:.3f}, LSE max abs {stats['lse_max_abs']:.3e}")
+        f"worst err/bound {stats['worst_ratio']:.3f}, LSE max abs {stats['lse_max_abs']:.3e}, "
+        f"exact result rounded to bf16: max abs {stats.get('bf16_rounding_max_abs', float('nan')):.3e}")
+    record(label, stats)
     assert stats["worst_ratio"] <= 1.0, f"{label}: elementwise O gate failed {stats}"
     assert stats["mean_abs"] <= mean_tol, f"{label}: mean abs gate failed {stats}"
     assert stats["lse_max_abs"] <= lse_tol, f"{label}: LSE gate failed {stats}"

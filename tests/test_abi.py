@@ -77,8 +77,12 @@ def test_attn_fwd_validation(lib):
         assert fwd(lib, dqk=dqk, dv=dv) == c["ATTN_ERR_HEADDIM"]
     assert fwd(lib, dtype=2) == c["ATTN_ERR_DTYPE"]
     assert fwd(lib, dtype=-1) == c["ATTN_ERR_DTYPE"]
-    for s in (math.nan, math.inf, -math.inf, -0.5):
+    for s in (math.nan, math.inf, -math.inf):
         assert fwd(lib, scale=s) == c["ATTN_ERR_SCALE"]
+    # any finite scale passes the scale check (negative ones too); the misaligned
+    # pointer then stops the call before any launch
+    for s in (-0.5, -0.0, 0.0, -1e30):
+        assert fwd(lib, scale=s, q=P + 8) == c["ATTN_ERR_ALIGN"]
     for name in ("q", "k", "v", "o", "lse"):
         assert fwd(lib, **{name: P + 8}) == c["ATTN_ERR_ALIGN"]
     assert fwd(lib, causal=2) == c["ATTN_ERR_ARG"]
@@ -122,6 +126,8 @@ def test_fwd_fp8_validation(lib):
     assert f(*a) == c["ATTN_ERR_HEADDIM"]
     a = list(base); a[14] = math.nan
     assert f(*a) == c["ATTN_ERR_SCALE"]
+    a = list(base); a[14] = -0.1; a[0] = P + 1   # negative scale accepted, alignment fails
+    assert f(*a) == c["ATTN_ERR_ALIGN"]
     a = list(base); a[0] = P + 1
     assert f(*a) == c["ATTN_ERR_ALIGN"]
     a = list(base); a[11] = 100
@@ -155,7 +161,19 @@ def test_attn_fwd_strided_validation(lib):
     assert strided(lib, ks=[1 << 41, 8192, 128]) == c["ATTN_ERR_SHAPE"]
     assert strided(lib, dqk=96, dv=96) == c["ATTN_ERR_HEADDIM"]
     assert strided(lib, dtype=5) == c["ATTN_ERR_DTYPE"]
-    assert strided(lib, scale=-2.0) == c["ATTN_ERR_SCALE"]
+    assert strided(lib, scale=math.inf) == c["ATTN_ERR_SCALE"]
+    assert strided(lib, scale=-2.0, o=P + 4) == c["ATTN_ERR_ALIGN"]     # negative scale accepted
+    # O elements sharing an address (many workgroups would write one row)
+    assert strided(lib, os_=[0, 8192, 128]) == c["ATTN_ERR_SHAPE"]       # batch stride 0, B = 2
+    assert strided(lib, os_=[32768, 0, 128]) == c["ATTN_ERR_SHAPE"]      # head stride 0, H = 4
+    assert strided(lib, os_=[32768, 8192, 64]) == c["ATTN_ERR_SHAPE"]    # rows overlap (d_v 128)
+    assert strided(lib, os_=[32768, 4096, 128]) == c["ATTN_ERR_SHAPE"]   # heads overlap rows
+    assert strided(lib, os_=[8192, 12288, 128], B=2, H=4) == c["ATTN_ERR_SHAPE"]  # H into B
+    # non-overlapping layouts pass the stride checks (stopped by the alignment check)
+    assert strided(lib, os_=[32768, 128, 512], o=P + 4) == c["ATTN_ERR_ALIGN"]  # BNHD
+    assert strided(lib, os_=[0, 8192, 128], B=1, o=P + 4) == c["ATTN_ERR_ALIGN"]  # B = 1: unused
+    assert strided(lib, os_=[8192, 16384, 128], o=P + 4) == c["ATTN_ERR_ALIGN"]  # [H, B, N, d]
+    assert strided(lib, os_=[8192, 65536, 128], o=P + 4) == c["ATTN_ERR_ALIGN"]  # gaps between
     assert strided(lib, qs=[32768, 8192, 132]) == c["ATTN_ERR_ALIGN"]     # 264-byte rows
     assert strided(lib, os_=[32772, 8192, 128]) == c["ATTN_ERR_ALIGN"]
     assert strided(lib, causal=3) == c["ATTN_ERR_ARG"]
@@ -177,6 +195,8 @@ def test_attn_bwd_validation(lib):
     assert f(*a) == c["ATTN_ERR_DTYPE"]
     a = list(base); a[16] = float("nan")
     assert f(*a) == c["ATTN_ERR_SCALE"]
+    a = list(base); a[16] = -0.1; a[0] = P + 4
+    assert f(*a) == c["ATTN_ERR_ALIGN"]
     for i in range(10):
         a = list(base)
         a[i] = P + 4
@@ -205,7 +225,8 @@ def test_attn_fwd_decode_validation(lib):
     for dqk, dv in ((192, 128), (64, 128), (96, 96)):
         assert dec(lib, dqk=dqk, dv=dv) == c["ATTN_ERR_HEADDIM"]
     assert dec(lib, dtype=3) == c["ATTN_ERR_DTYPE"]
-    assert dec(lib, scale=-1.0) == c["ATTN_ERR_SCALE"]
+    assert dec(lib, scale=math.nan) == c["ATTN_ERR_SCALE"]
+    assert dec(lib, scale=-1.0, o=P + 4) == c["ATTN_ERR_ALIGN"]   # negative scale accepted
     assert dec(lib, o=P + 4) == c["ATTN_ERR_ALIGN"]
     assert dec(lib, ws=P + 4, ws_bytes=1 << 30) == c["ATTN_ERR_ALIGN"]
     assert dec(lib, causal=2) == c["ATTN_ERR_ARG"]
@@ -239,3 +260,67 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.attn_fwd(q, q, q)
+
+
+class _FakeTensor:
+    """Stands in for a GPU tensor in the binding's argument checks (no device needed)."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True, is_cuda=True):
+        import torch
+
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = is_cuda
+        self._contig = contiguous
+
+    def is_contiguous(self):
+        return self._contig
+
+    def numel(self):
+        return math.prod(self.shape)
+
+
+def test_binding_output_checks():
+    import torch
+
+    from exact_attention_81_amd import binding as bd
+
+    dev = torch.device("cuda:0")
+    shape = (2, 3, 40, 64)
+    ok = _FakeTensor(shape, torch.bfloat16)
+    bd._check_output(ok, "out", shape, torch.bfloat16, dev)
+    bad = [
+        _FakeTensor((2, 3, 39, 64), torch.bfloat16),                  # too few rows
+        _FakeTensor((2, 3, 40, 128), torch.bfloat16),                 # wrong d
+        _FakeTensor(shape, torch.float16),                            # wrong dtype
+        _FakeTensor(shape, torch.bfloat16, device="cuda:1"),          # other device
+        _FakeTensor(shape, torch.bfloat16, is_cuda=False),            # host memory
+        _FakeTensor(shape, torch.bfloat16, contiguous=False),         # not dense
+    ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            bd._check_output(t, "out", shape, torch.bfloat16, dev)
+    # a strided out is allowed where the caller asks for it
+    bd._check_output(_FakeTensor(shape, torch.bfloat16, contiguous=False), "out", shape,
+                     torch.bfloat16, dev, dense=False)
+    lse = _FakeTensor((2, 3, 40), torch.float32)
+    bd._check_output(lse, "lse", (2, 3, 40), torch.float32, dev)
+    for t in (_FakeTensor((2, 3, 41), torch.float32), _FakeTensor((2, 3, 40), torch.bfloat16),
+              _FakeTensor((6, 40), torch.float32)):
+        with pytest.raises(ValueError):
+            bd._check_output(t, "lse", (2, 3, 40), torch.float32, dev)
+
+
+def test_binding_descale_checks():
+    import torch
+
+    from exact_attention_81_amd import binding as bd
+
+    dev = torch.device("cuda:0")
+    bd._check_vector(_FakeTensor((2, 3, 4), torch.float32), "q_descale", 24, torch.float32, dev)
+    for t in (_FakeTensor((2, 3, 3), torch.float32), _FakeTensor((2, 3, 4), torch.float16),
+              _FakeTensor((2, 3, 4), torch.float32, contiguous=False),
+              _FakeTensor((2, 3, 4), torch.float32, device="cuda:1")):
+        with pytest.raises(ValueError):
+            bd._check_vector(t, "q_descale", 24, torch.float32, dev)

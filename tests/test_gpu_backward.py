@@ -33,17 +33,18 @@ def gate(got, ref, label):
     assert worst <= 1.0, f"{label}: elementwise error {worst}"
 
 
-def run_case(B, H, nq, nkv, d, causal, seed, dtype=torch.bfloat16):
-    label = f"bwd B{B} H{H} Nq{nq} Nkv{nkv} d{d} causal={causal} {dtype} seed={seed}"
+def run_case(B, H, nq, nkv, d, causal, seed, dtype=torch.bfloat16, scale=None):
+    scale = d ** -0.5 if scale is None else scale
+    label = f"bwd B{B} H{H} Nq{nq} Nkv{nkv} d{d} causal={causal} {dtype} scale={scale:.4f} seed={seed}"
     log("start " + label)
     q, k, v = synth.qkv(B, H, nq, nkv, d, d, seed, dtype)
     g = torch.Generator("cpu").manual_seed(seed + 1)
     do = torch.randn((B, H, nq, d), generator=g, dtype=torch.float32).to(dtype)
     dq_, dk_, dv_, ddo = to_dev(q, k, v, do)
-    o, lse = ea.attn_fwd(dq_, dk_, dv_, causal=causal)
-    gq, gk, gv = ea.attn_bwd(dq_, dk_, dv_, o, lse, ddo, causal=causal)
+    o, lse = ea.attn_fwd(dq_, dk_, dv_, causal=causal, scale=scale)
+    gq, gk, gv = ea.attn_bwd(dq_, dk_, dv_, o, lse, ddo, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    rq, rk, rv, _ = oracle.attention_backward(q, k, v, do, d ** -0.5, causal)
+    rq, rk, rv, _ = oracle.attention_backward(q, k, v, do, scale, causal)
     for name, got, ref in (("dQ", gq, rq), ("dK", gk, rk), ("dV", gv, rv)):
         gate(f64(got), ref, f"{label} {name}")
     return gq, gk, gv
@@ -109,3 +110,9 @@ def test_backward_many_items(causal):
     """576 workgroups per kernel (more than the 256 compute units), heavy and light
     causal tiles mixed; every head checked."""
     run_case(2, 72, 512, 512, 128, causal, seed=3401 + int(causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_negative_scale(causal):
+    run_case(2, 3, 300, 300, 128, causal, seed=3301 + int(causal), scale=-128 ** -0.5)
+    run_case(1, 2, 100, 257, 64, causal, seed=3311 + int(causal), scale=-0.3)

@@ -16,16 +16,17 @@ from gpu_util import compare, f64, log, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_case(B, H, H_kv, nq, nkv, d, causal, seed, splits=0, dtype=torch.bfloat16):
+def run_case(B, H, H_kv, nq, nkv, d, causal, seed, splits=0, dtype=torch.bfloat16, scale=None):
     q, k, v = synth.qkv_gqa(B, H, H_kv, nq, nkv, d, seed, dtype)
     used = ea.attn_decode_splits(B, H, H_kv, nq, nkv, d, splits)
+    scale = d ** -0.5 if scale is None else scale
     label = (f"decode B{B} H{H} Hkv{H_kv} Nq{nq} Nkv{nkv} d{d} causal={causal} {dtype} "
-             f"splits={splits}->{used} seed={seed}")
+             f"splits={splits}->{used} scale={scale:.4f} seed={seed}")
     log("start " + label)
     dq, dk, dv = to_dev(q, k, v)
-    o, lse = ea.attn_fwd_decode(dq, dk, dv, causal=causal, num_splits=splits)
+    o, lse = ea.attn_fwd_decode(dq, dk, dv, causal=causal, num_splits=splits, scale=scale)
     torch.cuda.synchronize()
-    o_ref, lse_ref = oracle.attention_gqa(q, k, v, d ** -0.5, causal)
+    o_ref, lse_ref = oracle.attention_gqa(q, k, v, scale, causal)
     return compare(f64(o), f64(lse), o_ref, lse_ref, label)
 
 
@@ -118,3 +119,9 @@ def test_decode_workload_sampled():
         o_ref, lse_ref = oracle.head(q[b, h], k[b, h // g], v[b, h // g], w.scale, w.causal)
         compare(o[b, h], lse[b, h], o_ref, lse_ref, f"{w.label()} head ({b},{h})")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("splits", [1, 0, 5])
+def test_decode_negative_scale(splits):
+    run_case(2, 16, 2, 8, 1500, 128, True, seed=900 + splits, splits=splits, scale=-128 ** -0.5)
+    run_case(3, 16, 4, 8, 777, 64, False, seed=910 + splits, splits=splits, scale=-0.2)

@@ -83,3 +83,14 @@ def test_strided_rejects_bad_views():
     with pytest.raises(ea.AttnError):                  # 264-byte rows: not 16-byte aligned
         ea.attn_fwd(odd, k, v)
     np.testing.assert_equal(ea.attn_strerror(-6), "tensor pointer not 16-byte aligned")
+
+
+def test_bnhd_negative_scale():
+    dev = require_gpu()
+    q, k, v = synth.qkv(2, 4, 300, 300, 128, 128, seed=1234)
+    label = "BNHD negative scale causal"
+    log("start " + label)
+    o, lse = ea.attn_fwd(bnhd(q, dev), bnhd(k, dev), bnhd(v, dev), causal=True, scale=-0.1)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, -0.1, True)
+    compare(f64(o), f64(lse), o_ref, lse_ref, label)

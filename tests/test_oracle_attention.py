@@ -46,10 +46,10 @@ def brute_force(q, k, v, scale, causal):
     (1, 1, 1, 1, False), (3, 5, 2, 3, False), (5, 3, 4, 2, True), (4, 4, 3, 5, True),
     (2, 7, 8, 8, True), (8, 8, 8, 4, False), (7, 2, 2, 2, True),
 ])
-def test_brute_force_tiny(nq, nkv, dqk, dv, causal):
+@pytest.mark.parametrize("scale", [0.7, -0.45])
+def test_brute_force_tiny(nq, nkv, dqk, dv, causal, scale):
     rng = np.random.default_rng(nq * 100 + nkv * 10 + dqk + causal)
     q, k, v = rng.standard_normal((nq, dqk)) * 2, rng.standard_normal((nkv, dqk)), rng.standard_normal((nkv, dv))
-    scale = 0.7
     o, lse = oracle.head(q, k, v, scale, causal)
     ob, lb = brute_force(q, k, v, scale, causal)
     np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
@@ -110,6 +110,17 @@ def test_two_keys_sigmoid_form():
     w0 = 1.0 / (1.0 + np.exp(s1 - s0))
     np.testing.assert_allclose(o, w0[:, None] * v[0] + (1 - w0)[:, None] * v[1], atol=1e-14)
     np.testing.assert_allclose(lse, np.logaddexp(s0, s1), atol=1e-14)
+
+
+def test_negative_scale_prefers_the_smallest_score():
+    # A negative scale reverses the ordering of the scores: with scale -1 and
+    # scores q.k of ln 3 and 0, the weights are exp(-ln 3) : 1 = 1/4 : 3/4.
+    q = np.array([[1.0]])
+    k = np.array([[math.log(3.0)], [0.0]])
+    v = np.array([[4.0, -8.0], [0.0, 8.0]])
+    o, lse = oracle.head(q, k, v, -1.0, False)
+    np.testing.assert_allclose(o[0], [1.0, 4.0], atol=1e-15)
+    assert abs(lse[0] - math.log(4.0 / 3.0)) < 1e-15
 
 
 def test_hand_worked_example():

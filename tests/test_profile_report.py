@@ -47,21 +47,32 @@ def test_algorithmic_bytes():
     assert profile_report.algorithmic_bytes(f) == bh * (4096 * 128 * 3 + 4 * 3 * 32 + 2 * 4096 * 128 + 4 * 4096)
 
 
+TRACE_HEAD = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+
+
 def test_report_end_to_end(tmp_path):
     d = str(tmp_path)
     _write(f"{d}/stats/run_kernel_stats.csv",
            ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
-           [[KNAME.format(c="false"), 10, 1.3e6, 1.3e5, 60.0, 1.25e5, 1.4e5, 1.0],
-            [KNAME.format(c="true"), 10, 0.85e6, 0.85e5, 40.0, 0.8e5, 0.9e5, 1.0]])
-    head = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+           [[KNAME.format(c="false"), 2, 2.6e5, 1.3e5, 60.0, 1.25e5, 1.35e5, 1.0],
+            [KNAME.format(c="true"), 2, 1.7e5, 0.85e5, 40.0, 0.8e5, 0.9e5, 1.0]])
+    _write(f"{d}/stats/run_kernel_trace.csv", TRACE_HEAD,
+           [["KERNEL_DISPATCH", 1, KNAME.format(c="false"), 1000, 126000],
+            ["KERNEL_DISPATCH", 2, KNAME.format(c="true"), 130000, 210000],
+            ["KERNEL_DISPATCH", 3, KNAME.format(c="false"), 300000, 435000],
+            ["KERNEL_DISPATCH", 4, KNAME.format(c="true"), 440000, 530000]])
+    head = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     mib = 1024
     # the copy reads and writes 1 GiB; FETCH_SIZE shows half of it (as on the box)
     _write(f"{d}/fetch/run_counter_collection.csv", head,
-           [[COPY, "FETCH_SIZE", mib * 1024 / 2], [KNAME.format(c="false"), "FETCH_SIZE", 49000.0],
-            [KNAME.format(c="false"), "FETCH_SIZE", 50000.0], [KNAME.format(c="true"), "FETCH_SIZE", 74000.0]])
+           [[1, KNAME.format(c="false"), "FETCH_SIZE", 49000.0],
+            [2, KNAME.format(c="true"), "FETCH_SIZE", 74000.0],
+            [3, KNAME.format(c="false"), "FETCH_SIZE", 50000.0],
+            [4, COPY, "FETCH_SIZE", mib * 1024 / 2]])
     _write(f"{d}/write/run_counter_collection.csv", head,
-           [[COPY, "WRITE_SIZE", mib * 1024], [KNAME.format(c="false"), "WRITE_SIZE", 33280.0],
-            [KNAME.format(c="true"), "WRITE_SIZE", 33280.0]])
+           [[1, KNAME.format(c="false"), "WRITE_SIZE", 33280.0],
+            [2, KNAME.format(c="true"), "WRITE_SIZE", 33280.0],
+            [3, COPY, "WRITE_SIZE", mib * 1024]])
     w0 = synth.workload("single", causal=False)
     w1 = synth.workload("single", causal=True)
     bench = {"kernel_source_sha": "abc", "roofline": {"kernel": f"attn_fwd_kernel ({w0.label()})"},
@@ -86,8 +97,32 @@ def test_report_end_to_end(tmp_path):
     assert rec["kernel_source_sha"] == "abc"
     assert rec["dominant_variant"] == w0.label()
     assert rec["hbm_bytes_per_launch"] == 49500.0 * 1024 * 2 + 33280.0 * 1024
+    assert rec["trace_avg_us_per_variant"] == {w0.label(): 130.0, w1.label(): 85.0}
     text = open(f"{out}/attn_fwd_single.md").read()
-    assert "python3 bench.py" in text and "| 10 |" in text
+    assert "python3 bench.py" in text and "| 2 |" in text
+
+
+def test_variants_sharing_a_kernel_follow_launch_order():
+    """The target workload's three sequence lengths run the same kernel instance on the
+    same grid: dispatches are attributed by bench.py's launch order, and a trace that
+    does not follow it is refused."""
+    import pytest
+
+    ws = profile_report.workloads_of("target")
+    assert [w.N_q for w in ws] == [4096, 4096, 8192, 8192, 16384, 16384]
+    rows = []
+    for step in range(3):
+        for i, w in enumerate(ws):
+            rows.append({"Dispatch_Id": str(100 + 6 * step + i),
+                         "Kernel_Name": KNAME.format(c="true" if w.causal else "false")})
+    rows.insert(4, {"Dispatch_Id": "50", "Kernel_Name": COPY})  # other kernels are ignored
+    lab = profile_report.assign_variants(rows, ws)
+    assert len(lab) == 18
+    assert lab[100] == ws[0].label() and lab[104] == ws[4].label() and lab[117] == ws[5].label()
+    bad = [dict(r) for r in rows if r["Kernel_Name"] != COPY]
+    bad[1]["Kernel_Name"] = KNAME.format(c="false")   # two non-causal launches in a row
+    with pytest.raises(ValueError):
+        profile_report.assign_variants(bad, ws)
 
 
 def test_counter_report_end_to_end(tmp_path):
@@ -101,17 +136,21 @@ def test_counter_report_end_to_end(tmp_path):
     _write(f"{d}/p1/run_kernel_stats.csv",
            ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
            [[KNAME.format(c="false"), 2, 2 * dur_ns, dur_ns, 100.0, dur_ns, dur_ns, 0.0]])
-    head = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     k = KNAME.format(c="false")
+    kc = KNAME.format(c="true")
+    _write(f"{d}/p1/run_kernel_trace.csv", TRACE_HEAD,
+           [["KERNEL_DISPATCH", 1, k, 0, int(dur_ns)], ["KERNEL_DISPATCH", 2, kc, 200000, 290000]])
+    head = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     # 2.0 GHz for 125 us = 250000 cycles per XCD, summed over 8
     _write(f"{d}/p1/run_counter_collection.csv", head,
-           [[k, "MfmaUtil", 50.0], [k, "GRBM_GUI_ACTIVE", 8 * 250000.0], [k, "VALUBusy", 40.0],
-            [k, "LdsUtil", 20.0], [k, "LDSBankConflict", 0.0], [k, "LdsBankConflict", 0.0]])
+           [[1, k, "MfmaUtil", 50.0], [1, k, "GRBM_GUI_ACTIVE", 8 * 250000.0], [1, k, "VALUBusy", 40.0],
+            [1, k, "LdsUtil", 20.0], [1, k, "LDSBankConflict", 0.0], [1, k, "LdsBankConflict", 0.0],
+            [2, kc, "MfmaUtil", 30.0]])
     scores = 4 * 16 * 2048 * 2048
     _write(f"{d}/p2/run_counter_collection.csv", head,
-           [[k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", flops / 512], [k, "SQ_INSTS_VALU_TRANS_F32", scores / 64],
-            [k, "SQ_INSTS_VALU", 5 * scores / 64], [k, "SQ_VALU_MFMA_BUSY_CYCLES", 1000.0],
-            [k, "SQ_VALU_MFMA_COEXEC_CYCLES", 400.0]])
+           [[1, k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", flops / 512], [1, k, "SQ_INSTS_VALU_TRANS_F32", scores / 64],
+            [1, k, "SQ_INSTS_VALU", 5 * scores / 64], [1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 1000.0],
+            [1, k, "SQ_VALU_MFMA_COEXEC_CYCLES", 400.0], [2, kc, "SQ_INSTS_VALU", 1.0]])
     with open(f"{d}/commands.txt", "w") as fh:
         fh.write("rocprofv3 --pmc ...\n")
     import sys
@@ -123,8 +162,10 @@ def test_counter_report_end_to_end(tmp_path):
     finally:
         sys.argv = argv
     text = open(f"{d}/out/attn_fwd_single_counters.md").read()
-    rows = {r.split("|")[1].strip(): r.split("|")[2].strip() for r in text.splitlines()
-            if r.startswith("| ") and w.label() in text}
+    sect = text[text.index(w.label()):]
+    sect = sect[:sect.index("## ", 3)] if "## " in sect[3:] else sect
+    rows = {r.split("|")[1].strip(): r.split("|")[2].strip() for r in sect.splitlines()
+            if r.startswith("| ")}
     assert rows["executed / counted"] == "1.000"
     assert rows["shader clock"] == "2.000 GHz"
     assert rows["transcendental instructions per score"] == "1.000"
