@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_decode_splits,
     attn_fwd,
     attn_fwd_decode,
+    attn_fwd_decode_noalloc,
     attn_fwd_fp8,
     attn_fwd_tau,
     attn_quantize_fp8,

@@ -65,6 +65,11 @@ def load_library() -> ctypes.CDLL:
     lib.attn_decode_splits.restype = i
     lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i,
+                                            vp]
+    lib.attn_fwd_decode_noalloc.restype = i
+    lib.attn_decode_scratch_bytes.argtypes = []
+    lib.attn_decode_scratch_bytes.restype = ctypes.c_size_t
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_bwd.restype = i
     lib.attn_strerror.argtypes = [i]
@@ -334,6 +339,34 @@ def attn_fwd_decode(q, k, v, *, causal: bool = False, scale: Optional[float] = N
                              _ptr(workspace), ws_bytes, _stream(q))
     if rc != 0:
         raise AttnError(rc, "attn_fwd_decode")
+    return out, lse
+
+
+def attn_fwd_decode_noalloc(q, k, v, *, out, lse, causal: bool = False,
+                            scale: Optional[float] = None, num_splits: int = 0):
+    """attn_fwd_decode with the split partials in the library's static scratch: the C
+    call allocates nothing, and neither does this binding (``out`` [B,H,N_q,d] and
+    ``lse`` [B,H,N_q] float32 are the caller's)."""
+    import torch
+
+    _check(q, "q", (torch.bfloat16, torch.float16))
+    _check(k, "k", (q.dtype,), q.device)
+    _check(v, "v", (q.dtype,), q.device)
+    B, H, n_q, d = q.shape
+    H_kv, n_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, H_kv, n_kv, d) or v.shape != (B, H_kv, n_kv, v.shape[3]):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    d_v = v.shape[3]
+    _check_output(out, "out", (B, H, n_q, d_v), q.dtype, q.device)
+    _check_output(lse, "lse", (B, H, n_q), torch.float32, q.device)
+    if scale is None:
+        scale = d ** -0.5
+    dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_FP16
+    rc = load_library().attn_fwd_decode_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, n_q, n_kv, d, d_v,
+        float(scale), int(bool(causal)), dtype, int(num_splits), _stream(q))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_decode_noalloc")
     return out, lse
 
 

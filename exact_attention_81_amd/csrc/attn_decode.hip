@@ -23,6 +23,8 @@
 // refreshed only past 8 doublings. At the end the waves of a row block merge
 // their (m, l, O) states through LDS and write O and LSE (one split) or the
 // fp32 partial (O_s = O normalised by its own sum, LSE_s) of the split.
+#include <mutex>
+
 #include "device.h"
 #include "mfma16.h"
 #include "tile_io.h"
@@ -367,6 +369,36 @@ hipError_t launch_decode16(const DecodeParams& p, int d, bool causal, bool fp16,
   if (d == 64) return fp16 ? launch_d<64, true>(p, causal, stream) : launch_d<64, false>(p, causal, stream);
   if (d == 128) return fp16 ? launch_d<128, true>(p, causal, stream) : launch_d<128, false>(p, causal, stream);
   return hipErrorInvalidValue;
+}
+
+// ---- Static scratch for callers that cannot allocate (attn_fwd_decode_noalloc).
+// The split partials of a call live in this file-scope device array instead of a
+// caller-supplied workspace. Every GPU the library runs on holds its own copy until
+// the process ends. In host code `scratch` only names the symbol: its device address
+// on the current GPU comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 int decode_resident_workgroups(int d) {

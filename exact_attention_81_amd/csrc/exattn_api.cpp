@@ -314,6 +314,29 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v,
+                            float scale, int causal, int dtype, int num_splits, void* stream) {
+  // The same checks as attn_fwd_decode, in the same order, before the scratch is sized.
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (int rc = check_decode(B, H, H_kv, N_q, N_kv, d_qk, d_v)) return rc;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_DTYPE;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  const int splits = attn_decode_splits(B, H, H_kv, N_q, N_kv, d_qk, d_v, num_splits);
+  if (splits < 0) return splits;
+  const size_t need = decode_workspace(B, H, N_q, d_v, splits);
+  if (need > exattn::decode_scratch_bytes()) return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need && exattn::decode_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  return attn_fwd_decode(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d_qk, d_v, scale, causal, dtype,
+                         num_splits, ws, need, stream);
+}
+
+size_t attn_decode_scratch_bytes(void) { return exattn::decode_scratch_bytes(); }
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N_q,
              int N_kv, int d_qk, int d_v, float scale, int causal, int dtype, void* stream) {
@@ -359,6 +382,9 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP kernel launch failed";
     case ATTN_ERR_ARG: return "argument out of range";
+    case ATTN_ERR_SCRATCH:
+      return "the split partials need more than the library's static decode scratch "
+             "(attn_decode_scratch_bytes(); pass a workspace to attn_fwd_decode instead)";
     default: return "unknown error code";
   }
 }

@@ -69,6 +69,10 @@ hipError_t launch_decode16(const DecodeParams& p, int d, bool causal, bool fp16,
 hipError_t launch_bwd16(const BwdParams& p, int d, bool causal, bool fp16, hipStream_t stream);
 // Decode workgroups the current device runs at once for head dim d (0 if unknown).
 int decode_resident_workgroups(int d);
+// The library's static decode scratch: its size, and its device address on the current
+// device (looked up once per device with hipGetSymbolAddress; never allocates).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_quantize_fp8(const void* x, uint8_t* x8, float* descale, int B, int H,
                                int N, const float* signs, bool transpose_out,
                                hipStream_t stream);

@@ -54,7 +54,9 @@ enum {
     ATTN_ERR_SCALE = -5,   /* scale is NaN or infinite */
     ATTN_ERR_ALIGN = -6,   /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_HIP = -7,     /* the kernel launch failed (hipGetLastError) */
-    ATTN_ERR_ARG = -8      /* another argument is out of range (tau, transpose flag) */
+    ATTN_ERR_ARG = -8,     /* another argument is out of range (tau, transpose flag) */
+    ATTN_ERR_SCRATCH = -9  /* attn_fwd_decode_noalloc: the problem needs more scratch
+                              than the library's static buffer holds */
 };
 
 /*
@@ -216,6 +218,30 @@ int attn_decode_splits(int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int 
  * size is < 1.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int N_q, int d_v, int splits);
+
+/*
+ * attn_fwd_decode_noalloc - attn_fwd_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Arguments, checks and results are attn_fwd_decode's
+ * with the same num_splits; the split partials go to a scratch buffer the
+ * library holds as a static device array (one per GPU, kept until the process
+ * ends) instead of a caller workspace. The call allocates and frees nothing.
+ *
+ *   The partials need splits * B*H*N_q * (d_v + 1) * 4 bytes (splits as
+ *   attn_decode_splits reports); more than attn_decode_scratch_bytes() (8 MiB)
+ *   returns ATTN_ERR_SCRATCH before anything is launched. A call with one
+ *   split uses no scratch.
+ *   The scratch needs no initial contents (every partial is written before it
+ *   is read). All calls on one GPU share it: calls that overlap in time on one
+ *   GPU (other streams, other host threads) race and give wrong results;
+ *   serialise them, or use attn_fwd_decode with separate workspaces.
+ */
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N_q, int N_kv, int d_qk, int d_v,
+                            float scale, int causal, int dtype, int num_splits, void* stream);
+
+/* attn_decode_scratch_bytes - size of the static scratch attn_fwd_decode_noalloc uses. */
+size_t attn_decode_scratch_bytes(void);
 
 /*
  * attn_bwd - gradients of attn_fwd: dQ, dK, dV from Q, K, V, the forward's O and

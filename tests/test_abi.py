@@ -40,8 +40,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert names == ["attn_bwd", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd",
-                     "attn_fwd_decode", "attn_fwd_fp8", "attn_fwd_strided", "attn_fwd_tau",
+    assert names == ["attn_bwd", "attn_decode_scratch_bytes", "attn_decode_splits",
+                     "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_decode",
+                     "attn_fwd_decode_noalloc", "attn_fwd_fp8", "attn_fwd_strided", "attn_fwd_tau",
                      "attn_quantize_fp8", "attn_strerror"]
     for n in names:
         assert hasattr(lib, n), n
@@ -324,3 +325,35 @@ def test_binding_descale_checks():
               _FakeTensor((2, 3, 4), torch.float32, device="cuda:1")):
         with pytest.raises(ValueError):
             bd._check_vector(t, "q_descale", 24, torch.float32, dev)
+
+
+def noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=8, Hkv=2, Nq=1, Nkv=4096, dqk=128, dv=128,
+             scale=0.1, causal=0, dtype=0, splits=4)
+    a.update(kw)
+    return lib.attn_fwd_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                       a["Hkv"], a["Nq"], a["Nkv"], a["dqk"], a["dv"], a["scale"],
+                                       a["causal"], a["dtype"], a["splits"], None)
+
+
+def test_attn_fwd_decode_noalloc_validation(lib):
+    """The allocation-free decode entry point checks what attn_fwd_decode checks, in the
+    same order, and refuses problems whose split partials exceed its static scratch
+    (before any device call)."""
+    c = codes()
+    assert lib.attn_decode_scratch_bytes() == 8 << 20
+    for name in ("q", "k", "v", "o", "lse"):
+        assert noalloc(lib, **{name: None}) == c["ATTN_ERR_NULL"]
+    assert noalloc(lib, B=0) == c["ATTN_ERR_SHAPE"]
+    assert noalloc(lib, H=6, Hkv=4) == c["ATTN_ERR_SHAPE"]
+    assert noalloc(lib, dqk=192) == c["ATTN_ERR_HEADDIM"]
+    assert noalloc(lib, dtype=3) == c["ATTN_ERR_DTYPE"]
+    assert noalloc(lib, scale=math.inf) == c["ATTN_ERR_SCALE"]
+    assert noalloc(lib, o=P + 4) == c["ATTN_ERR_ALIGN"]
+    assert noalloc(lib, causal=2) == c["ATTN_ERR_ARG"]
+    assert noalloc(lib, splits=-1) == c["ATTN_ERR_ARG"]
+    # 256 splits of B8 H64 N_q1 d128 need 256 * 512 * 129 * 4 bytes = 64.5 MiB > 8 MiB
+    need = lib.attn_decode_workspace_bytes(8, 64, 1, 128, 256)
+    assert need > lib.attn_decode_scratch_bytes()
+    assert noalloc(lib, B=8, H=64, Hkv=8, Nkv=16384, splits=256) == c["ATTN_ERR_SCRATCH"]
+    assert "scratch" in ea.attn_strerror(c["ATTN_ERR_SCRATCH"])
