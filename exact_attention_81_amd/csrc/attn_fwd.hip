@@ -225,24 +225,27 @@ void attn_fwd_kernel(const FwdParams p) {
 
   // S(j): S^T = K_j Q^T into sacc. Operands are read one K-step ahead of the products;
   // the scheduling fences keep the compiler from hoisting every read above the first
-  // product (16 live fragments).
-  auto s_phase = [&](auto stage) {
+  // product (16 live fragments). The first K-step's fragments come in as arguments: in
+  // the unrolled loop they are read during the last products of the PV phase before
+  // (K(j) is already in LDS then), so the S phase does not open with a full LDS
+  // latency in which the SIMD's other wave is in its softmax (+0.6 % measured).
+  auto kread = [&](auto stage, int s_, int kb) {
     const lds_u8* st = k_lds + int(stage) * K_STAGE;
+    const int rows = (2 * s_ + half < KA_D / 8) ? kb * 32 * KA_ROW : kb * 32 * KB_ROW;
+    return lds_read128(st + koff[s_] + rows);
+  };
+  u32x4_t kpre0, kpre1;  // K-step 0 of the next S phase, read during the PV phase
+  auto s_phase_from = [&](auto stage, u32x4_t kf0, u32x4_t kf1) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-    auto kread = [&](int s_, int kb) {
-      const int rows = (2 * s_ + half < KA_D / 8) ? kb * 32 * KA_ROW : kb * 32 * KB_ROW;
-      return lds_read128(st + koff[s_] + rows);
-    };
-    u32x4_t kf0 = kread(0, 0), kf1 = kread(0, 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t nf0 = kf0, nf1 = kf1;
       if (s + 1 < KS) {
-        nf0 = kread(s + 1, 0);
-        nf1 = kread(s + 1, 1);
+        nf0 = kread(stage, s + 1, 0);
+        nf1 = kread(stage, s + 1, 1);
       }
       sacc[0] = E::mfma(kf0, qf[s], sacc[0]);
       sacc[1] = E::mfma(kf1, qf[s], sacc[1]);
@@ -251,13 +254,16 @@ void attn_fwd_kernel(const FwdParams p) {
       kf1 = nf1;
     }
   };
+  auto s_phase = [&](auto stage) { s_phase_from(stage, kread(stage, 0, 0), kread(stage, 0, 1)); };
 
   // PV(j): O^T += V_j^T P_j^T from pf. A transposing LDS read takes longer than one
   // product, so operands are read PV_AHEAD products ahead (the S accumulators are dead
-  // here, which leaves room for the extra fragments).
+  // here, which leaves room for the extra fragments). `k_next` is the ring stage of the
+  // next S phase's K tile (its first fragments go to kpre0/kpre1 near the end), or
+  // std::false_type for none.
   constexpr int PV_STEPS = 4 * DB;
   constexpr int PV_AHEAD = 3;
-  auto pv_phase = [&](auto stage, auto hook) {
+  auto pv_phase = [&](auto stage, auto hook, auto k_next) {
     lds_u8* const lds0 = (lds_u8*)(uintptr_t)0;  // voff holds absolute LDS addresses
     const lds_u8* st = lds0 + int(stage) * V_STAGE;
     auto vread = [&](int step) {
@@ -276,9 +282,16 @@ void attn_fwd_kernel(const FwdParams p) {
       if (step + PV_AHEAD < PV_STEPS) vf[step % PV_AHEAD] = vread(step + PV_AHEAD);
       oacc[step % DB] = E::mfma(cur, pf[step / DB], oacc[step % DB]);
       hook(step);
+      if constexpr (!std::is_same_v<decltype(k_next), std::false_type>) {
+        if (step == PV_STEPS - 3) {
+          kpre0 = kread(k_next, 0, 0);
+          kpre1 = kread(k_next, 0, 1);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  constexpr std::false_type NO_K{};
   auto no_hook = [](int) {};
 
   // sm(j): masking (MASK: a key of the tile is past N_kv or past this wave's diagonal),
@@ -445,8 +458,8 @@ void attn_fwd_kernel(const FwdParams p) {
       pin_p();
       tile_barrier<LOADS_PER_TILE>();
     }
-    pv_phase(v_prev, spread_issue(j, k_next, v_next));
-    s_phase(k_cur);
+    pv_phase(v_prev, spread_issue(j, k_next, v_next), k_cur);
+    s_phase_from(k_cur, kpre0, kpre1);
   };
   // The same with stages computed at run time (tiles that need masking, and the few
   // iterations that do not fill a group of three).
@@ -463,7 +476,7 @@ void attn_fwd_kernel(const FwdParams p) {
       pin_p();
       barrier_and_issue(j, (r + 2) % NSTAGE, (r + 1) % NSTAGE);
     }
-    if (active(j - 1)) pv_phase((r + 2) % NSTAGE, no_hook);
+    if (active(j - 1)) pv_phase((r + 2) % NSTAGE, no_hook, NO_K);
     if (active(j)) s_phase(r);
   };
   if (ntiles > 0) {
@@ -497,7 +510,7 @@ void attn_fwd_kernel(const FwdParams p) {
       if (wave_plain(ntiles - 1)) softmax(ntiles - 1, PLAIN); else softmax(ntiles - 1, MASKED);
     }
     if (!group_b) tile_barrier<LOADS_PER_TILE>();
-    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE, no_hook);
+    if (active(ntiles - 1)) pv_phase((ntiles - 1) % NSTAGE, no_hook, NO_K);
   }
 
   __builtin_amdgcn_s_waitcnt(0x0070);  // no LDS fill may be in flight when the waves end
