@@ -1,4 +1,5 @@
-"""Builds libexattn.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libexattn.so (HIP, gfx950) in-tree with hipcc, and the separate unit-rate
+probe library libexattn_probes.so (see unit_probes.py; libexattn.so never loads it).
 
     python -m exact_attention_81_amd.build
 
@@ -25,6 +26,8 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_fp8.hip", "attn_decode.hip", "attn_bwd.hip"]
 HOST_SOURCES = ["exattn_api.cpp"]
+PROBE_SOURCES = ["unit_probes.hip"]
+PROBE_LIB_NAME = "libexattn_probes.so"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",
           "-Wno-inline-asm"]
@@ -47,10 +50,33 @@ def _run(cmd):
     return r
 
 
+def _link(cc, objs, tmp, name):
+    out = os.path.join(PKG, name)
+    tmp_out = os.path.join(tmp, name)
+    _run([cc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-o", tmp_out])
+    shutil.copyfile(tmp_out, out + ".tmp")
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compile the unit-rate probes into libexattn_probes.so; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="exattn_probes_") as tmp:
+        objs = []
+        for src in PROBE_SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            _run([cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        out = _link(cc, objs, tmp, PROBE_LIB_NAME)
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libexattn.so; returns its path."""
     cc = hipcc()
-    out = os.path.join(PKG, LIB_NAME)
     with tempfile.TemporaryDirectory(prefix="exattn_build_") as tmp:
         objs = []
         for src in HIP_SOURCES:
@@ -62,10 +88,7 @@ def build(verbose: bool = False) -> str:
             _run([cc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-c",
                   os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
-        tmp_out = os.path.join(tmp, LIB_NAME)
-        _run([cc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-o", tmp_out])
-        shutil.copyfile(tmp_out, out + ".tmp")
-        os.replace(out + ".tmp", out)
+        out = _link(cc, objs, tmp, LIB_NAME)
     if verbose:
         print(f"built {out}")
     return out
@@ -73,3 +96,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probes(verbose=True)

@@ -1,0 +1,259 @@
+// Unit-rate probes for gfx950 that the attention kernels' design rests on (a separate
+// library, libexattn_probes.so; nothing in libexattn.so calls it):
+//
+//  * exp_fma: independent chains of v_exp_f32 and of unpacked v_fma_f32, issued in a
+//    fixed interleaved order by one or two waves per SIMD. It tells whether the
+//    hardware exponential runs beside the FMAs (then moving exponentials onto FMAs,
+//    "FlashAttention 3 and 4: When the Bottleneck Moves" section 3.2, could pay) or
+//    shares their issue (then it cannot).
+//  * lds: LDS read throughput per compute unit for ds_read_b128 and the transposing
+//    ds_read_b64_tr_b16, alone and with a stream of v_mfma_f32_32x32x16_bf16 in the same
+//    wave, at one and two waves per SIMD: how fast one wave can feed its matrix core
+//    from LDS.
+//
+// Every probe runs one workgroup per compute unit. Each wave stamps the start and end
+// of its loop with the shader clock (s_memtime) and the 100 MHz real-time counter
+// (s_memrealtime); a workgroup's time is the span from its first wave's start to its
+// last wave's end (waves that share a SIMD need not finish together: the oldest may
+// run ahead), averaged over all workgroups.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+namespace probes {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) unsigned char lds_b;
+
+constexpr int kExpFmaIter = 4096;
+constexpr int kLdsIter = 2048;
+constexpr int kMaxThreads = 512;
+constexpr int kPadFloats = 24576;  // 96 KB
+
+// Lane 0 of every wave writes its loop's start and end stamps: 4 values per wave,
+// kMaxThreads / 64 wave slots per workgroup.
+__device__ inline void stamp(long long* clk, long long t0, long long t1, long long w0, long long w1) {
+  if ((threadIdx.x & 63) == 0) {
+    long long* c = clk + ((size_t)blockIdx.x * (kMaxThreads / 64) + threadIdx.x / 64) * 4;
+    c[0] = t0;
+    c[1] = t1;
+    c[2] = w0;
+    c[3] = w1;
+  }
+}
+
+// NE exponential chains and NF FMA chains per lane; the volatile asm statements keep
+// the issue order fixed: exponential i sits at slot round(i (NE + NF) / NE).
+template <int NE, int NF>
+__global__ __launch_bounds__(512) void exp_fma_kernel(float* out, float a, float b,
+                                                      long long* clk) {
+  float e[NE > 0 ? NE : 1], f[NF > 0 ? NF : 1];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) e[i] = 0.5f + 0.001f * i + 0.0001f * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NF; ++i) f[i] = 0.5f - 0.001f * i + 0.0001f * threadIdx.x;
+  const long long t0 = clock64(), w0 = wall_clock64();
+  for (int it = 0; it < kExpFmaIter; ++it) {
+    constexpr int N = NE + NF;
+    int ie = 0, jf = 0;
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+      const bool do_exp = NE > 0 && ie < NE && (NF == 0 || s * NE >= ie * N);
+      if (do_exp) {
+        asm volatile("v_exp_f32 %0, %0" : "+v"(e[ie]));
+        ++ie;
+      } else if (jf < NF) {
+        asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(f[jf]) : "v"(a), "v"(b));
+        ++jf;
+      }
+    }
+  }
+  const long long t1 = clock64(), w1 = wall_clock64();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) sum += e[i];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) sum += f[i];
+  // 96 KB of LDS per workgroup: no compute unit can hold two of them.
+  __shared__ float pad[kPadFloats];
+  pad[(threadIdx.x * 48) % kPadFloats] = sum;
+  __syncthreads();
+  out[blockIdx.x * blockDim.x + threadIdx.x] = pad[(threadIdx.x * 48 + 48) % kPadFloats];
+  stamp(clk, t0, t1, w0, w1);
+}
+
+// MODE 0: ds_read_b128; 1: two ds_read_b64_tr_b16 per step; 2: MFMA only;
+// 3: MFMA + ds_read_b128; 4: MFMA + two tr reads. 8 steps per iteration; every read
+// stays inside the 64 KB the workgroup holds, conflict-free within a wave.
+template <int MODE>
+__global__ __launch_bounds__(512) void lds_kernel(unsigned* out, long long* clk) {
+  // 96 KB (one workgroup per compute unit); the loop reads the first 64 KB.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[98304];
+  const int t = threadIdx.x;
+  for (int i = t; i < 65536 / 4; i += blockDim.x) ((unsigned*)lds)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = t & 63, wave = t >> 6;
+  const unsigned base = (wave * 4096 + lane * 16) & 0xFFFF;
+  u32x4_t acc = {0, 0, 0, 0};
+  f32x16_t c0 = {}, c1 = {};
+  const u32x4_t a = {(unsigned)t, 1u, 2u, 3u};
+  lds_b* const lds0 = (lds_b*)0;
+  const long long t0 = clock64(), w0 = wall_clock64();
+  for (int it = 0; it < kLdsIter; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const unsigned addr = (base + u * 1024 + (it & 7) * 8192) & 0xFFF0;
+      if constexpr (MODE == 0 || MODE == 3) {
+        acc ^= *(const __attribute__((address_space(3))) u32x4_t*)(lds0 + addr);
+      }
+      if constexpr (MODE == 1 || MODE == 4) {
+        const unsigned a2 = addr & 0xFFF8;
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(lds0 + a2));
+        const i16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(lds0 + (a2 ^ 2048)));
+        acc[0] ^= (unsigned)(__builtin_bit_cast(unsigned long long, v1) & 0xFFFFFFFFu);
+        acc[1] ^= (unsigned)(__builtin_bit_cast(unsigned long long, v2) >> 32);
+      }
+      if constexpr (MODE >= 2) {
+        if (u & 1)
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, a), c1, 0, 0, 0);
+        else
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, a), c0, 0, 0, 0);
+      }
+    }
+  }
+  const long long t1 = clock64(), w1 = wall_clock64();
+  float sum = 0.f;
+  for (int r = 0; r < 16; ++r) sum += c0[r] + c1[r];
+  out[blockIdx.x * blockDim.x + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ __float_as_uint(sum);
+  stamp(clk, t0, t1, w0, w1);
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+// Launches `launch` twice (the first warms up) on `blocks` workgroups of `threads` and
+// returns the mean span in shader cycles from a workgroup's first wave start to its
+// last wave end, and the shader clock in GHz.
+template <typename F>
+int timed(F launch, int blocks, int threads, double* cycles, double* ghz) {
+  if (threads <= 0 || threads > kMaxThreads || threads % 64) return -4;
+  const int waves = threads / 64;
+  const size_t nclk = (size_t)blocks * (kMaxThreads / 64) * 4;
+  float* out = nullptr;
+  long long* clk = nullptr;
+  if (hipMalloc(&out, (size_t)blocks * threads * 4) != hipSuccess) return -1;
+  if (hipMalloc(&clk, nclk * 8) != hipSuccess) {
+    (void)hipFree(out);
+    return -1;
+  }
+  int rc = 0;
+  for (int rep = 0; rep < 2 && rc == 0; ++rep) {
+    launch(out, clk);
+    if (hipDeviceSynchronize() != hipSuccess) rc = -2;
+  }
+  std::vector<long long> h(nclk);
+  if (rc == 0 && hipMemcpy(h.data(), clk, nclk * 8, hipMemcpyDeviceToHost) != hipSuccess) rc = -3;
+  (void)hipFree(out);
+  (void)hipFree(clk);
+  if (rc) return rc;
+  double c = 0, w = 0;
+  for (int i = 0; i < blocks; ++i) {
+    const long long* b = h.data() + (size_t)i * (kMaxThreads / 64) * 4;
+    long long c0 = b[0], c1 = b[1], r0 = b[2], r1 = b[3];
+    for (int v = 1; v < waves; ++v) {
+      c0 = std::min(c0, b[4 * v]);
+      c1 = std::max(c1, b[4 * v + 1]);
+      r0 = std::min(r0, b[4 * v + 2]);
+      r1 = std::max(r1, b[4 * v + 3]);
+    }
+    c += (double)(c1 - c0);
+    w += (double)(r1 - r0);
+  }
+  *cycles = c / blocks;
+  *ghz = (c / blocks) / ((w / blocks) * 10.0);  // wall_clock64 ticks at 100 MHz
+  return 0;
+}
+
+template <int NE, int NF>
+int run_exp_fma(int waves_per_simd, double* out3) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  const int threads = 256 * waves_per_simd;  // one workgroup per CU, waves_per_simd per SIMD
+  double cyc = 0, ghz = 0;
+  const int rc = timed([&](float* o, long long* clk) {
+    hipLaunchKernelGGL((exp_fma_kernel<NE, NF>), dim3(cus), dim3(threads), 0, 0, o, 1.0001f, 0.001f, clk);
+  }, cus, threads, &cyc, &ghz);
+  if (rc) return rc;
+  out3[0] = cyc / ((double)kExpFmaIter * (NE + NF) * waves_per_simd);  // cycles per wave instr per SIMD
+  out3[1] = ghz;
+  out3[2] = cyc;
+  return 0;
+}
+
+template <int MODE>
+int run_lds(int waves_per_simd, double* out3) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  const int threads = 256 * waves_per_simd;
+  double cyc = 0, ghz = 0;
+  const int rc = timed([&](float* o, long long* clk) {
+    hipLaunchKernelGGL((lds_kernel<MODE>), dim3(cus), dim3(threads), 0, 0, (unsigned*)o, clk);
+  }, cus, threads, &cyc, &ghz);
+  if (rc) return rc;
+  const double waves = threads / 64.0, steps = (double)kLdsIter * 8;
+  out3[0] = (MODE == 2) ? 0.0 : steps * waves * 1024.0 / cyc;                  // LDS bytes/clk/CU
+  out3[1] = (MODE >= 2) ? cyc / (steps * waves_per_simd) : 0.0;                // cycles per MFMA per SIMD
+  out3[2] = ghz;
+  return 0;
+}
+
+}  // namespace probes
+
+extern "C" {
+
+// Cycles per wave instruction per SIMD (out[0]), shader clock in GHz (out[1]) and loop
+// cycles (out[2]) for `ne` exponential and `nf` FMA chains per lane, interleaved, at
+// `waves_per_simd` (1 or 2) waves per SIMD. Supported (ne, nf): (8,0) (0,8) (0,16) (8,8)
+// (8,16) (8,24) (16,16). Returns 0, or a negative code (unsupported pair, HIP failure).
+int probe_exp_fma(int ne, int nf, int waves_per_simd, double* out) {
+  if (!out || waves_per_simd < 1 || waves_per_simd > 2) return -4;
+  if (ne == 8 && nf == 0) return probes::run_exp_fma<8, 0>(waves_per_simd, out);
+  if (ne == 0 && nf == 8) return probes::run_exp_fma<0, 8>(waves_per_simd, out);
+  if (ne == 0 && nf == 16) return probes::run_exp_fma<0, 16>(waves_per_simd, out);
+  if (ne == 8 && nf == 8) return probes::run_exp_fma<8, 8>(waves_per_simd, out);
+  if (ne == 8 && nf == 16) return probes::run_exp_fma<8, 16>(waves_per_simd, out);
+  if (ne == 8 && nf == 24) return probes::run_exp_fma<8, 24>(waves_per_simd, out);
+  if (ne == 16 && nf == 16) return probes::run_exp_fma<16, 16>(waves_per_simd, out);
+  return -4;
+}
+
+// LDS bytes per clock per CU (out[0]), cycles per MFMA per SIMD (out[1], MFMA modes) and
+// the shader clock (out[2]) for `mode` (0: ds_read_b128, 1: ds_read_b64_tr_b16 pairs,
+// 2: MFMA only, 3: MFMA + b128 read, 4: MFMA + tr pair) at 1 or 2 waves per SIMD.
+int probe_lds(int mode, int waves_per_simd, double* out) {
+  if (!out || waves_per_simd < 1 || waves_per_simd > 2) return -4;
+  switch (mode) {
+    case 0: return probes::run_lds<0>(waves_per_simd, out);
+    case 1: return probes::run_lds<1>(waves_per_simd, out);
+    case 2: return probes::run_lds<2>(waves_per_simd, out);
+    case 3: return probes::run_lds<3>(waves_per_simd, out);
+    case 4: return probes::run_lds<4>(waves_per_simd, out);
+    default: return -4;
+  }
+}
+
+}  // extern "C"

@@ -48,6 +48,17 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_is_separate_and_exports_its_probes(lib):
+    from exact_attention_81_amd import unit_probes
+
+    if not os.path.exists(unit_probes.LIB_PATH):
+        pytest.skip("libexattn_probes.so not built")
+    probes = unit_probes.load()          # loads only; no probe is run without a GPU
+    for n in unit_probes.SYMBOLS:
+        assert hasattr(probes, n), n
+        assert not hasattr(lib, n), n    # the attention library does not carry them
+
+
 def test_strerror_covers_codes(lib):
     c = codes()
     for name, val in c.items():
