@@ -89,7 +89,11 @@ __global__ __launch_bounds__(512) void exp_fma_kernel(float* out, float a, float
 
 // MODE 0: ds_read_b128; 1: two ds_read_b64_tr_b16 per step; 2: MFMA only;
 // 3: MFMA + ds_read_b128; 4: MFMA + two tr reads. 8 steps per iteration; every read
-// stays inside the 64 KB the workgroup holds, conflict-free within a wave.
+// stays inside the 64 KB the workgroup holds, conflict-free within a wave. In modes
+// 0-4 an iteration's reads are consumed in the same iteration (the loop drains them
+// at its end); modes 5 and 6 keep reads in flight across iterations:
+// 5: ds_read_b128 through a ring of 8 registers (a read is consumed 8 reads after its
+//    issue); 6: MFMA whose A operand is the ds_read_b128 issued 4 products earlier.
 template <int MODE>
 __global__ __launch_bounds__(512) void lds_kernel(unsigned* out, long long* clk) {
   // 96 KB (one workgroup per compute unit); the loop reads the first 64 KB.
@@ -103,8 +107,41 @@ __global__ __launch_bounds__(512) void lds_kernel(unsigned* out, long long* clk)
   f32x16_t c0 = {}, c1 = {};
   const u32x4_t a = {(unsigned)t, 1u, 2u, 3u};
   lds_b* const lds0 = (lds_b*)0;
+  auto rd = [&](unsigned addr) { return *(const __attribute__((address_space(3))) u32x4_t*)(lds0 + addr); };
+  auto step_addr = [&](int it, int u) { return (base + u * 1024 + (it & 7) * 8192) & 0xFFF0; };
+  u32x4_t ring[8];
+  if constexpr (MODE == 5 || MODE == 6) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ring[u] = rd(step_addr(0, u));
+  }
   const long long t0 = clock64(), w0 = wall_clock64();
-  for (int it = 0; it < kLdsIter; ++it) {
+  if constexpr (MODE == 5) {
+    for (int it = 1; it <= kLdsIter; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc ^= ring[u];
+        ring[u] = rd(step_addr(it, u));
+        __builtin_amdgcn_sched_barrier(0);  // keep the program order: 8 reads in flight
+      }
+    }
+  }
+  if constexpr (MODE == 6) {
+    for (int it = 1; it <= kLdsIter; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4_t op = ring[u & 3];
+        ring[u & 3] = rd(step_addr(it, u));
+        if (u & 1)
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
+                                                       __builtin_bit_cast(bf16x8_t, a), c1, 0, 0, 0);
+        else
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
+                                                       __builtin_bit_cast(bf16x8_t, a), c0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the program order: reads 4 products ahead
+      }
+    }
+  }
+  for (int it = 0; it < (MODE <= 4 ? kLdsIter : 0); ++it) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const unsigned addr = (base + u * 1024 + (it & 7) * 8192) & 0xFFF0;
@@ -133,6 +170,10 @@ __global__ __launch_bounds__(512) void lds_kernel(unsigned* out, long long* clk)
   const long long t1 = clock64(), w1 = wall_clock64();
   float sum = 0.f;
   for (int r = 0; r < 16; ++r) sum += c0[r] + c1[r];
+  if constexpr (MODE == 5 || MODE == 6) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= ring[u];
+  }
   out[blockIdx.x * blockDim.x + t] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ __float_as_uint(sum);
   stamp(clk, t0, t1, w0, w1);
 }
@@ -216,7 +257,8 @@ int run_lds(int waves_per_simd, double* out3) {
   if (rc) return rc;
   const double waves = threads / 64.0, steps = (double)kLdsIter * 8;
   out3[0] = (MODE == 2) ? 0.0 : steps * waves * 1024.0 / cyc;                  // LDS bytes/clk/CU
-  out3[1] = (MODE >= 2) ? cyc / (steps * waves_per_simd) : 0.0;                // cycles per MFMA per SIMD
+  constexpr bool kMfma = MODE == 2 || MODE == 3 || MODE == 4 || MODE == 6;
+  out3[1] = kMfma ? cyc / (steps * waves_per_simd) : 0.0;                       // cycles per MFMA per SIMD
   out3[2] = ghz;
   return 0;
 }
@@ -243,7 +285,8 @@ int probe_exp_fma(int ne, int nf, int waves_per_simd, double* out) {
 
 // LDS bytes per clock per CU (out[0]), cycles per MFMA per SIMD (out[1], MFMA modes) and
 // the shader clock (out[2]) for `mode` (0: ds_read_b128, 1: ds_read_b64_tr_b16 pairs,
-// 2: MFMA only, 3: MFMA + b128 read, 4: MFMA + tr pair) at 1 or 2 waves per SIMD.
+// 2: MFMA only, 3: MFMA + b128 read, 4: MFMA + tr pair, 5: b128 reads kept 8 in flight,
+// 6: MFMA fed by the b128 read issued 4 products earlier) at 1 or 2 waves per SIMD.
 int probe_lds(int mode, int waves_per_simd, double* out) {
   if (!out || waves_per_simd < 1 || waves_per_simd > 2) return -4;
   switch (mode) {
@@ -252,6 +295,8 @@ int probe_lds(int mode, int waves_per_simd, double* out) {
     case 2: return probes::run_lds<2>(waves_per_simd, out);
     case 3: return probes::run_lds<3>(waves_per_simd, out);
     case 4: return probes::run_lds<4>(waves_per_simd, out);
+    case 5: return probes::run_lds<5>(waves_per_simd, out);
+    case 6: return probes::run_lds<6>(waves_per_simd, out);
     default: return -4;
   }
 }

@@ -12,7 +12,9 @@ Two questions the attention kernels' design depends on:
   * How fast can a wave read LDS, alone and beside its own matrix-core stream? Bytes
     per clock per CU for ds_read_b128 and ds_read_b64_tr_b16, and cycles per
     v_mfma_f32_32x32x16_bf16 when every product is fed by 1 KB of LDS reads in the
-    same wave, at one and two waves per SIMD.
+    same wave, at one and two waves per SIMD; with the reads drained every 8 steps, and
+    with reads kept in flight across steps (8 deep, or 4 products ahead of the
+    product that uses them).
 
 Needs a GPU; the library is built by ``build.build_probes()``.
 """
@@ -29,7 +31,8 @@ SYMBOLS = ("probe_exp_fma", "probe_lds")
 
 EXP_FMA_MIXES = ((8, 0), (0, 8), (0, 16), (8, 8), (8, 16), (8, 24), (16, 16))
 LDS_MODES = {0: "ds_read_b128", 1: "ds_read_b64_tr_b16 x2", 2: "mfma 32x32x16 bf16 only",
-             3: "mfma + ds_read_b128", 4: "mfma + ds_read_b64_tr_b16 x2"}
+             3: "mfma + ds_read_b128", 4: "mfma + ds_read_b64_tr_b16 x2",
+             5: "ds_read_b128, 8 in flight", 6: "mfma fed by ds_read_b128 issued 4 ahead"}
 
 
 def load() -> ctypes.CDLL:
@@ -66,7 +69,8 @@ def run() -> dict:
             bpc, mfma_cyc, ghz = _call(lib.probe_lds, mode, wps)
             res["lds"].append({"waves_per_simd": wps, "mode": name,
                                "lds_bytes_per_clk_cu": bpc if mode != 2 else None,
-                               "cycles_per_mfma": mfma_cyc if mode >= 2 else None, "ghz": ghz})
+                               "cycles_per_mfma": mfma_cyc if mode in (2, 3, 4, 6) else None,
+                               "ghz": ghz})
     return res
 
 
