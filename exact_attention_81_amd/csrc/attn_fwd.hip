@@ -221,6 +221,8 @@ void attn_fwd_kernel(const FwdParams p) {
   u32x4_t pf[4];             // P^T B operands of a tile between its softmax and PV phases
   float m_ref = -INFINITY;   // running reference max, log2 units
   float l_part = 0.f;        // this lane's partial row sum
+  float tile_alpha = 1.f;    // a tile's re-base factor of O, applied in its PV phase
+  bool tile_rebased = false; // some row of the wave re-based in the tile's softmax
   const float c = p.scale_log2;
 
   // S(j): S^T = K_j Q^T into sacc. Operands are read one K-step ahead of the products;
@@ -258,7 +260,11 @@ void attn_fwd_kernel(const FwdParams p) {
 
   // PV(j): O^T += V_j^T P_j^T from pf. A transposing LDS read takes longer than one
   // product, so operands are read PV_AHEAD products ahead (the S accumulators are dead
-  // here, which leaves room for the extra fragments). `k_next` is the ring stage of the
+  // here, which leaves room for the extra fragments). A re-base in the tile's softmax
+  // reaches O here, before the first product, behind a wave-uniform branch. The same
+  // multiplies inside the softmax's branch, where S (and at d_qk = 192 twelve Q
+  // fragments) are live too, cost 56 more registers at d = 128 and made the compiler
+  // spill 16-18 at d_qk = 192 (1.7 % slower on B1 H16 N8192 causal). `k_next` is the ring stage of the
   // next S phase's K tile (its first fragments go to kpre0/kpre1 near the end), or
   // std::false_type for none.
   constexpr int PV_STEPS = 4 * DB;
@@ -273,6 +279,12 @@ void attn_fwd_kernel(const FwdParams p) {
       const u32x2_t hi = lds_read_tr16(a + 8 * V_ROW);
       return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
     };
+    if (__builtin_amdgcn_readfirstlane((int)tile_rebased)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= tile_alpha;
+    }
     u32x4_t vf[PV_AHEAD];
 #pragma unroll
     for (int i = 0; i < PV_AHEAD; ++i) vf[i] = vread(i);
@@ -298,6 +310,7 @@ void attn_fwd_kernel(const FwdParams p) {
   // row max, conditional rescale, exponentials, row sum; sacc -> pf.
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    tile_rebased = false;
     // Row r of key block kb is key j*BLOCK_N + kb*32 + 8*(r>>2) + 4*half + (r&3); it is
     // visible iff its tile-local offset kb*32 + 8*(r>>2) + (r&3) (a constant) is at most
     // `room`. Comparing constants against one per-tile value keeps the mask from
@@ -337,8 +350,9 @@ void attn_fwd_kernel(const FwdParams p) {
       }
       return ps;
     };
-    // Row max and the rescale of the running state when it grew by more than TAU
-    // doublings; true when any row of the wave re-based (wave-uniform).
+    // Row max and the re-base of the running state when it grew by more than TAU
+    // doublings (l here, O in the PV phase); true when any row of the wave re-based
+    // (wave-uniform).
     auto rebase = [&]() {
       float mx = sacc[0][0];
 #pragma unroll
@@ -353,10 +367,8 @@ void attn_fwd_kernel(const FwdParams p) {
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
       m_ref = grow ? mt : m_ref;
       l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      tile_alpha = alpha;
+      tile_rebased = true;
       return true;
     };
     auto neg_ref = [&]() { return m_ref == -INFINITY ? 0.f : -m_ref; };

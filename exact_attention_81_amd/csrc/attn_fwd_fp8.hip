@@ -204,6 +204,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   float m_ref = -INFINITY;   // running reference max, log2 units (bias excluded)
   float l_row = 0.f;         // the query's row sum (the same in both lane halves)
   float tile_inv_ratio = 1.f;  // dv_ref / dv of the tile between its softmax and PV
+  float tile_alpha = 1.f;      // the tile's re-base factor for O, applied in its PV phase
 
   // S(j): S^T = K_j Q^T. Operands are read one product ahead of their MFMA.
   auto s_phase = [&](auto stage) {
@@ -230,6 +231,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   // PV(j): O^T += V_j^T P_j^T, operands two products ahead; hook(step) issues tile loads.
   // The row sum of the rounded P comes from two more products, ones^T P^T (every A
   // byte 1.0 in e4m3, 0x38), issued with the first PV products and read at the end.
+  // The softmax's re-base factor is applied to each accumulator block right before its
+  // first product of the tile, on every tile (a factor of 1 when no row grew, which is
+  // exact). A wave-uniform branch around 64 multiplies in the softmax instead splits the
+  // accumulators' live ranges, and the kernel spilled 56-68 B per lane around it.
   auto pv_phase = [&](auto stage, auto hook) {
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
     constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
@@ -247,6 +252,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     for (int step = 0; step < STEPS; ++step) {
       const i32x8_t cur = vf[step % 2];
       if (step + 2 < STEPS) vf[step % 2] = vread(step + 2);
+      if (step < 4) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[step][r] *= tile_alpha;
+      }
       oacc[step % 4] = mfma_f8(cur, pf[step / 4], oacc[step % 4]);
       if (step < NKC) lsum = mfma_f8(ones, pf[step], lsum);
       hook(step);
@@ -286,15 +295,9 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     mx = max_halves(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * ct;
     const bool grow = mt > m_ref + (float)F8_TAU;
-    if (__any(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
-      m_ref = grow ? mt : m_ref;
-      l_row *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
+    tile_alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mt) : 1.f;
+    m_ref = grow ? mt : m_ref;
+    l_row *= tile_alpha;
     const float nm = ((m_ref == -INFINITY) ? 0.f : -m_ref) + F8_PBIAS + vbias;
     unsigned w[NKB][4];
 #pragma unroll
