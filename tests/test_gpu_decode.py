@@ -125,3 +125,88 @@ def test_decode_workload_sampled():
 def test_decode_negative_scale(splits):
     run_case(2, 16, 2, 8, 1500, 128, True, seed=900 + splits, splits=splits, scale=-128 ** -0.5)
     run_case(3, 16, 4, 8, 777, 64, False, seed=910 + splits, splits=splits, scale=-0.2)
+
+
+def _decode_ws_bytes(B, H, nq, d, splits):
+    return ea.load_library().attn_decode_workspace_bytes(B, H, nq, d, splits)
+
+
+def test_decode_workspace_leftover_bytes_and_reuse():
+    """Whatever bytes the split workspace holds on entry (zeros, all ones, random bytes,
+    another call's partials) the result is the same, bit for bit, and calls that reuse
+    one workspace, also with other shapes, agree with fresh ones."""
+    B, H, H_kv, nq, nkv, d = 2, 16, 4, 3, 2100, 128
+    q, k, v = synth.qkv_gqa(B, H, H_kv, nq, nkv, d, seed=941)
+    dq, dk, dv = to_dev(q, k, v)
+    splits = ea.attn_decode_splits(B, H, H_kv, nq, nkv, d, 6)
+    assert splits == 6
+    need = _decode_ws_bytes(B, H, nq, d, splits)
+    nwords = (need + 3) // 4
+    log(f"start decode workspace fills B{B} H{H} Hkv{H_kv} Nq{nq} Nkv{nkv} splits={splits}")
+    ref_o, ref_l = ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_gqa(q, k, v, d ** -0.5, True)
+    compare(f64(ref_o), f64(ref_l), o_ref, lse_ref, "decode reference call")
+    gen = torch.Generator().manual_seed(942)
+    fills = {
+        "zeros": torch.zeros(nwords, dtype=torch.int32),
+        "ones": torch.full((nwords,), -1, dtype=torch.int32),
+        "random": torch.randint(-2 ** 31, 2 ** 31 - 1, (nwords,), dtype=torch.int32, generator=gen),
+    }
+    for name, fill in fills.items():
+        ws = fill.to(dq.device).view(torch.float32)
+        for rep in range(3):   # the same workspace again: its counters carry over
+            o, l = ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref_o) and torch.equal(l, ref_l), (name, rep)
+    # another shape through the same workspace, then the first again
+    q2, k2, v2 = synth.qkv_gqa(1, 8, 8, 1, 3000, 128, seed=943)
+    d2q, d2k, d2v = to_dev(q2, k2, v2)
+    s2 = ea.attn_decode_splits(1, 8, 8, 1, 3000, 128, 11)
+    assert _decode_ws_bytes(1, 8, 1, 128, s2) <= need
+    o2, l2 = ea.attn_fwd_decode(d2q, d2k, d2v, num_splits=11, workspace=ws)
+    o, l = ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    o2_ref, l2_ref = oracle.attention_gqa(q2, k2, v2, 128 ** -0.5, False)
+    compare(f64(o2), f64(l2), o2_ref, l2_ref, "decode second shape, shared workspace")
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_decode_graph_replays():
+    """attn_fwd_decode (split kernel and merge kernel) captured in a HIP graph: every
+    replay, on new inputs copied into the captured buffers, is checked against an eager
+    call on the same inputs, with eager work and synchronisations between the replays.
+    The call issues no memset."""
+    B, H, H_kv, nq, nkv, d = 2, 8, 2, 2, 2500, 128
+    splits = 5
+    dev = torch.device("cuda:0")
+    q0, k0, v0 = synth.qkv_gqa(B, H, H_kv, nq, nkv, d, seed=951)
+    dq, dk, dv = to_dev(q0, k0, v0)
+    out = torch.empty((B, H, nq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(((_decode_ws_bytes(B, H, nq, d, splits) + 3) // 4,), dtype=torch.float32,
+                     device=dev)
+    log("start decode graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream, as torch asks
+        ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        qn, kn, vn = synth.qkv_gqa(B, H, H_kv, nq, nkv, d, seed=952 + rep)
+        dq.copy_(qn.to(dev)); dk.copy_(kn.to(dev)); dv.copy_(vn.to(dev))
+        torch.cuda.synchronize()
+        log(f"decode graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        e_o, e_l = ea.attn_fwd_decode(dq, dk, dv, causal=True, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_o) and torch.equal(lse, e_l), rep
+        if rep == 0:
+            o_ref, lse_ref = oracle.attention_gqa(qn, kn, vn, d ** -0.5, True)
+            compare(f64(out), f64(lse), o_ref, lse_ref, "decode graph replay 0")
