@@ -18,6 +18,11 @@
 // the transposed ones, and P / dS fed from the accumulator registers in the
 // row order the transposing reads reproduce. Tiles go straight from global memory
 // into LDS (buffer_load ... lds), double-buffered, one workgroup barrier per tile.
+// Within a tile, LDS operands are read two products ahead of their MFMA, and the
+// elementwise steps run between the products that do not need them (P beside the
+// dP products, dS beside the dV products). Tiles whose scores are all visible take
+// a body without any mask test; the masked body only runs on ragged and (causal)
+// diagonal tiles, in a loop of its own.
 #include "device.h"
 #include "mfma16.h"
 #include "tile_io.h"
@@ -201,6 +206,70 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
   TrOffsets<D> tro(lane);
   const int limit = CAUSAL ? min(p.Nkv - 1, my_q + offset) : p.Nkv - 1;
+  const float nl = -lse2;
+
+  // One 32-key block: S^T = K Q^T, then dP^T = V dO^T with P^T = exp2(c S^T - LSE
+  // log2 e) computed beside those products, then dQ^T += K^T dS^T with dS^T = P^T (dP^T
+  // - D) computed beside the first of them. A operands are read two products ahead.
+  // Register r is key key0 + 8 (r/4) + 4 half + r%4.
+  auto key_block = [&](const lds_u8* kt, const lds_u8* vt, int kb, int key0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PER = 16 / KS;  // weights computed beside each dP product
+    f32x16_t s_acc, dp_acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
+    // operand stream of the S then dP products (step < KS: K rows, else V rows)
+    auto opa = [&](int step) { return row_operand<D>(step < KS ? kt : vt, 32 * kb, l32, half, step % KS); };
+    u32x4_t a[2] = {opa(0), opa(1)};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4_t cur = a[s % 2];
+      a[s % 2] = opa(s + 2);
+      s_acc = E::mfma(cur, qf[s], s_acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int room = limit - key0 - 4 * half;
+    constexpr int QSTEPS = 2 * DB;  // dQ products: step = ks * DB + db
+    auto tra = [&](int step) { return tr_operand<D>(kt, tro, step % DB, 32 * kb + 16 * (step / DB)); };
+    u32x4_t t[2];
+    float pr[16];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int step = KS + s;
+      const u32x4_t cur = a[step % 2];
+      if (step + 2 < 2 * KS)
+        a[step % 2] = opa(step + 2);
+      else
+        t[step + 2 - 2 * KS] = tra(step + 2 - 2 * KS);  // the first dQ operands
+      dp_acc = E::mfma(cur, dof[s], dp_acc);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int r = s * PER + i;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, nl));
+        pr[r] = (!MASK || (r >> 2) * 8 + (r & 3) <= room) ? x : 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto ds2 = [&](int w) {  // dS^T registers 2 w, 2 w + 1, packed
+      return E::pack2(pr[2 * w] * (dp_acc[2 * w] - dval), pr[2 * w + 1] * (dp_acc[2 * w + 1] - dval));
+    };
+    u32x4_t dsf[2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dsf[0][w] = ds2(w);
+#pragma unroll
+    for (int step = 0; step < QSTEPS; ++step) {
+      const u32x4_t cur = t[step % 2];
+      if (step + 2 < QSTEPS) t[step % 2] = tra(step + 2);
+      dqacc[step % DB] = E::mfma(cur, dsf[step / DB], dqacc[step % DB]);
+      if (step < DB) {
+#pragma unroll
+        for (int w = step * 4 / DB; w < (step + 1) * 4 / DB; ++w) dsf[1][w] = ds2(4 + w);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  constexpr std::false_type PLAIN{};
+  constexpr std::true_type MASKED{};
 
   lds_u8* const kl = (lds_u8*)smem;
   lds_u8* const vl = (lds_u8*)smem + 2 * TILE;
@@ -208,46 +277,33 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams
     load_tile<D, BN>(kl, kg, 0, p.Nkv, wave, lane);
     load_tile<D, BN>(vl, vg, 0, p.Nkv, wave, lane);
   }
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j & 1;
-    wait_all_and_barrier();  // tile j is in LDS; every wave is done with tile j - 1
-    if (j + 1 < ntiles) {
-      load_tile<D, BN>(kl + (st ^ 1) * TILE, kg, (j + 1) * BN, p.Nkv, wave, lane);
-      load_tile<D, BN>(vl + (st ^ 1) * TILE, vg, (j + 1) * BN, p.Nkv, wave, lane);
-    }
-    if (CAUSAL && j * BN > wave_last_key) continue;  // no key of the tile is visible
-    const lds_u8* kt = kl + st * TILE;
-    const lds_u8* vt = vl + st * TILE;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T = K Q^T and dP^T = V dO^T for keys j*64 + 32 kb + (accumulator rows).
-      f32x16_t s_acc, dp_acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        s_acc = E::mfma(row_operand<D>(kt, 32 * kb, l32, half, s), qf[s], s_acc);
-        dp_acc = E::mfma(row_operand<D>(vt, 32 * kb, l32, half, s), dof[s], dp_acc);
+  // Tiles before j_split have no key that some query of the workgroup misses; the rest
+  // (the ragged tail, causal: the diagonal) take the masked body. The two ranges run as
+  // two loops (one body each keeps the register allocation of each body on its own).
+  const int wg_plain_key = CAUSAL ? min(p.Nkv - 1, q0 + offset) : p.Nkv - 1;
+  const int j_split = min(ntiles, max(0, (wg_plain_key + 1) / BN));
+  auto tile_loop = [&](int from, int to, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int j = from; j < to; ++j) {
+      const int st = j & 1;
+      wait_all_and_barrier();  // tile j is in LDS; every wave is done with tile j - 1
+      if (j + 1 < ntiles) {
+        load_tile<D, BN>(kl + (st ^ 1) * TILE, kg, (j + 1) * BN, p.Nkv, wave, lane);
+        load_tile<D, BN>(vl + (st ^ 1) * TILE, vg, (j + 1) * BN, p.Nkv, wave, lane);
       }
-      // P^T and dS^T; register r is key j*64 + 32 kb + 8 (r/4) + 4 half + r%4.
-      const int room = limit - (j * BN + 32 * kb) - 4 * half;
-      f32x16_t ds_acc;
+      if (CAUSAL && j * BN > wave_last_key) continue;  // no key of the tile is visible
+      const lds_u8* kt = kl + st * TILE;
+      const lds_u8* vt = vl + st * TILE;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool vis = (r >> 2) * 8 + (r & 3) <= room;
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse2)) : 0.f;
-        ds_acc[r] = pr * (dp_acc[r] - dval);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key0 = j * BN + 32 * kb;
+        // masked range: skip blocks past N_kv or past the wave's last visible key
+        if (!MASK || (key0 < p.Nkv && (!CAUSAL || key0 <= wave_last_key))) key_block(kt, vt, kb, key0, mask_tag);
       }
-      u32x4_t dsf[2];
-      pack_rows<F16>(ds_acc, dsf);
-      // dQ^T += K^T dS^T over the block's 32 keys.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dqacc[db] = E::mfma(tr_operand<D>(kt, tro, db, 32 * kb + 16 * ks), dsf[ks], dqacc[db]);
     }
-  }
+  };
+  tile_loop(0, j_split, PLAIN);
+  tile_loop(j_split, ntiles, MASKED);
   __builtin_amdgcn_s_waitcnt(0x0070);
   if (my_q < p.Nq) {
     const float sc = p.scale;
@@ -331,62 +387,122 @@ __global__ __launch_bounds__(64 * KV_WAVES) void attn_bwd_dkdv_kernel(const BwdP
   const float c = p.scale_log2;
   const bool key_ok = my_k < p.Nkv;
 
-  for (int qt = qt0; qt < qt1; ++qt) {
-    const int st = (qt - qt0) & 1;
-    wait_all_and_barrier();  // tile qt is in LDS; every wave is done with tile qt - 1
-    if (qt + 1 < qt1) issue(qt + 1, st ^ 1);
-    const int qa = qt * BQ + 32 * qh;  // this wave's 32 queries
-    // Causal: none of this wave's queries sees any of its keys (i sees j iff j <= i + offset).
-    if (CAUSAL && qa + 31 + offset < wk0) continue;
-    const lds_u8* s = ring + st * STAGE;
-    const lds_u8* qtile = s;
-    const lds_u8* dtile = s + QTILE;
-    typedef const __attribute__((address_space(3))) float lds_f32;
+  // One tile of the wave's 32 queries: S = Q K^T, then dP = dO V^T with P = exp2(c S -
+  // LSE log2 e) computed beside those products, then dV^T += dO^T P with dS = P (dP - D)
+  // computed beside them, then dK^T += Q^T dS. Operands are read two products ahead.
+  // Register r is query qa + 8 (r/4) + 4 half + r%4.
+  //
+  // Without a mask, keys past N_kv (zero rows of K and V) only reach their own columns of
+  // dK and dV, which are never stored, and queries past N_q (zero rows of Q and dO, LSE
+  // and D read as 0) add exact zeros. A query with LSE = -inf sees no key, which only
+  // happens under the causal mask, so such rows only occur in masked tiles.
+  auto q_tile = [&](const lds_u8* qtile, int qa, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PER = 16 / KS;  // weights computed beside each dP product
+    const lds_u8* dtile = qtile + QTILE;
     typedef const __attribute__((address_space(3))) f32x4_t lds_f32x4;
-    lds_f32* lse_t = (lds_f32*)(s + 2 * QTILE) + 32 * qh;
-    lds_f32* del_t = (lds_f32*)(s + 2 * QTILE + 1024) + 32 * qh;
-
-    // S = Q K^T and dP = dO V^T: rows = the wave's 32 queries, column = this lane's key.
+    lds_f32x4* lse_t = (lds_f32x4*)(qtile + 2 * QTILE + 128 * qh + 16 * half);
+    lds_f32x4* del_t = (lds_f32x4*)(qtile + 2 * QTILE + 1024 + 128 * qh + 16 * half);
     f32x16_t s_acc, dp_acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s_acc[r] = dp_acc[r] = 0.f;
+    // operand stream of the S then dP products (step < KS: Q and K rows, else dO and V)
+    auto opa = [&](int step) { return row_operand<D>(step < KS ? qtile : dtile, 32 * qh, l32, half, step % KS); };
+    auto opb = [&](int step) { return row_operand<D>(step < KS ? kl : vl, 32 * kw, l32, half, step % KS); };
+    u32x4_t a[2] = {opa(0), opa(1)}, b[2] = {opb(0), opb(1)};
+    f32x4_t lz[4], dz[4];
 #pragma unroll
     for (int sk = 0; sk < KS; ++sk) {
-      const u32x4_t kb = row_operand<D>(kl, 32 * kw, l32, half, sk);
-      const u32x4_t vb = row_operand<D>(vl, 32 * kw, l32, half, sk);
-      s_acc = E::mfma(row_operand<D>(qtile, 32 * qh, l32, half, sk), kb, s_acc);
-      dp_acc = E::mfma(row_operand<D>(dtile, 32 * qh, l32, half, sk), vb, dp_acc);
-    }
-    // Register r is query qa + 8 (r/4) + 4 half + r%4: 4 consecutive queries per r/4.
-    f32x16_t p_acc, ds_acc;
+      const u32x4_t ca = a[sk % 2], cb = b[sk % 2];
+      a[sk % 2] = opa(sk + 2);
+      b[sk % 2] = opb(sk + 2);
+      s_acc = E::mfma(ca, cb, s_acc);
+      if (sk == 0) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int qi = 8 * g + 4 * half;
-      const f32x4_t lz = *(lds_f32x4*)(lse_t + qi);
-      const f32x4_t dz = *(lds_f32x4*)(del_t + qi);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        const int q = qa + qi + i;
-        // Visible: the key exists, the query exists and (causal) j <= i + offset.
-        const bool vis = key_ok && q < p.Nq && (!CAUSAL || my_k <= q + offset) && lz[i] != -INFINITY;
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lz[i] * 1.4426950408889634f)) : 0.f;
-        p_acc[r] = pr;
-        ds_acc[r] = pr * (dp_acc[r] - dz[i]);
+        for (int g = 0; g < 4; ++g) lz[g] = lse_t[2 * g];  // queries 8 g + 4 half .. + 3
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // causal: query qa + 8 (r/4) + 4 half + r%4 sees this lane's key iff
+    // 8 (r/4) + r%4 >= my_k - offset - qa - 4 half
+    const int tq = my_k - offset - qa - 4 * half;
+    constexpr int STEPS = 2 * DB;  // transposed-operand products: step = ks * DB + db
+    auto tra = [&](const lds_u8* tile, int step) {
+      return tr_operand<D>(tile, tro, step % DB, 32 * qh + 16 * (step / DB));
+    };
+    u32x4_t t[2];
+    float pr[16];
+#pragma unroll
+    for (int sk = 0; sk < KS; ++sk) {
+      const int step = KS + sk;
+      const u32x4_t ca = a[step % 2], cb = b[step % 2];
+      if (step + 2 < 2 * KS) {
+        a[step % 2] = opa(step + 2);
+        b[step % 2] = opb(step + 2);
+      } else {
+        t[step + 2 - 2 * KS] = tra(dtile, step + 2 - 2 * KS);  // the first dV operands
+      }
+      dp_acc = E::mfma(ca, cb, dp_acc);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int r = sk * PER + i;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, lz[r >> 2][r & 3] * -1.4426950408889634f));
+        pr[r] = (!MASK || (r >> 2) * 8 + (r & 3) >= tq) ? x : 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dz[g] = del_t[2 * g];
     u32x4_t pf[2], dsf[2];
-    pack_rows<F16>(p_acc, pf);
-    pack_rows<F16>(ds_acc, dsf);
-    // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dvacc[db] = E::mfma(tr_operand<D>(dtile, tro, db, 32 * qh + 16 * ks), pf[ks], dvacc[db]);
-        dkacc[db] = E::mfma(tr_operand<D>(qtile, tro, db, 32 * qh + 16 * ks), dsf[ks], dkacc[db]);
-      }
+      for (int w = 0; w < 4; ++w) pf[h][w] = E::pack2(pr[8 * h + 2 * w], pr[8 * h + 2 * w + 1]);
+    auto ds2 = [&](int w) {  // dS registers 2 w, 2 w + 1, packed
+      const int r = 2 * w;
+      return E::pack2(pr[r] * (dp_acc[r] - dz[r >> 2][r & 3]), pr[r + 1] * (dp_acc[r + 1] - dz[r >> 2][(r & 3) + 1]));
+    };
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+      const u32x4_t cur = t[step % 2];
+      t[step % 2] = step + 2 < STEPS ? tra(dtile, step + 2) : tra(qtile, step + 2 - STEPS);
+      dvacc[step % DB] = E::mfma(cur, pf[step / DB], dvacc[step % DB]);
+#pragma unroll
+      for (int w = step * 8 / STEPS; w < (step + 1) * 8 / STEPS; ++w) dsf[w / 4][w % 4] = ds2(w);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+      const u32x4_t cur = t[step % 2];
+      if (step + 2 < STEPS) t[step % 2] = tra(qtile, step + 2);
+      dkacc[step % DB] = E::mfma(cur, dsf[step / DB], dkacc[step % DB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  constexpr std::false_type PLAIN{};
+  constexpr std::true_type MASKED{};
+
+  // Causal: the query tiles before qt_split hold some query that misses some key of the
+  // workgroup; from qt_split on every query sees all 128 keys. The two ranges run as two
+  // loops (one body each keeps the register allocation of each body on its own).
+  int qt_split = qt0;
+  if (CAUSAL) {
+    const int x = k0 + BK - 1 - offset;  // first query that sees the workgroup's last key
+    qt_split = x <= 0 ? qt0 : min(qt1, max(qt0, (x + BQ - 1) / BQ));
   }
+  auto tile_loop = [&](int from, int to, auto mask_tag) __attribute__((always_inline)) {
+    for (int qt = from; qt < to; ++qt) {
+      const int st = (qt - qt0) & 1;
+      wait_all_and_barrier();  // tile qt is in LDS; every wave is done with tile qt - 1
+      if (qt + 1 < qt1) issue(qt + 1, st ^ 1);
+      const int qa = qt * BQ + 32 * qh;  // this wave's 32 queries
+      // Causal: none of this wave's queries sees any of its keys (i sees j iff j <= i + offset).
+      if (CAUSAL && qa + 31 + offset < wk0) continue;
+      q_tile(ring + st * STAGE, qa, mask_tag);
+    }
+  };
+  if (CAUSAL) tile_loop(qt0, qt_split, MASKED);
+  tile_loop(qt_split, qt1, PLAIN);
   // The two waves of a key block add their partial sums through LDS.
   wait_all_and_barrier();  // every wave is done with the tiles
   float* const sums = (float*)smem + kw * (2 * DB * 16 * 64);

@@ -253,7 +253,9 @@ size_t attn_decode_scratch_bytes(void);
  *
  *   q, k, v, o, dout, dq, dk, dv   dense [B, H, N, d], dtype; o and lse as attn_fwd
  *                                  wrote them for the same q, k, v, scale, causal
- *   lse    [B, H, N_q] float32 (rows with LSE = -inf get zero gradients)
+ *   lse    [B, H, N_q] float32, as attn_fwd wrote it; a row with no visible key
+ *          (LSE = -inf, causal with N_q > N_kv) gets zero gradients. An LSE of -inf
+ *          on a row that sees keys is outside this contract (non-finite results).
  *   delta  [B, H, N_q] float32 workspace: D is written there (caller-owned)
  *   d_qk = d_v = 64 or 128, else ATTN_ERR_HEADDIM.
  *   dq, dk, dv are fully written (rounded to nearest even); the result is
