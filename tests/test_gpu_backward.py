@@ -14,7 +14,7 @@ import torch
 import exact_attention_81_amd as ea
 import oracle
 from exact_attention_81_amd import synth
-from gpu_util import f64, log, to_dev
+from gpu_util import f64, log, record, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,8 @@ def gate(got, ref, label):
     worst = float((err / (2e-2 * scale + 2.0 ** -7 * np.abs(ref) + 1e-30)).max())
     log(f"{label}: rel Frobenius {fro:.3e}, max abs {err.max():.3e} (max |ref| {scale:.3e}), "
         f"worst err/bound {worst:.3f}")
+    record(label, dict(rel_frobenius=float(fro), max_abs=float(err.max()), max_ref=float(scale),
+                       worst_over_bound=worst))
     assert np.all(np.isfinite(got)), f"{label}: non-finite gradient"
     assert fro <= REL_FRO, f"{label}: relative Frobenius error {fro}"
     assert worst <= 1.0, f"{label}: elementwise error {worst}"
