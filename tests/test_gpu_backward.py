@@ -55,7 +55,7 @@ def run_case(B, H, nq, nkv, d, causal, seed, dtype=torch.bfloat16, scale=None):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 128, 128, 64), (2, 3, 300, 300, 128), (2, 2, 100, 333, 128),
                                    (1, 2, 257, 129, 64), (1, 4, 1024, 1024, 128), (1, 1, 1, 1, 64),
-                                   (2, 2, 31, 95, 64)],
+                                   (2, 2, 31, 95, 64), (1, 2, 700, 300, 128), (1, 2, 300, 700, 128)],
                          ids=lambda s: "B{}H{}_{}x{}_d{}".format(*s))
 def test_backward(shape, causal):
     B, H, nq, nkv, d = shape
