@@ -10,6 +10,10 @@
 //    ds_read_b64_tr_b16, alone and with a stream of v_mfma_f32_32x32x16_bf16 in the same
 //    wave, at one and two waves per SIMD: how fast one wave can feed its matrix core
 //    from LDS.
+//  * stream_read: HBM read bandwidth of a plain streaming kernel (16-byte loads over a
+//    1 GiB buffer, grid-stride, a given number of loads in flight per thread and
+//    workgroups per CU), the reference for kernels bound by their reads, such as the
+//    split-KV decode.
 //
 // Every probe runs one workgroup per compute unit. Each wave stamps the start and end
 // of its loop with the shader clock (s_memtime) and the 100 MHz real-time counter
@@ -263,6 +267,67 @@ int run_lds(int waves_per_simd, double* out3) {
   return 0;
 }
 
+// Every thread reads 16-byte chunks i = tid, tid + T, ... of the buffer (T threads in
+// the grid), U chunks per loop iteration kept in flight, and folds them into one word
+// so that no load can be dropped; the folded words go to `out`.
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, size_t n16,
+                                                          unsigned* __restrict__ out) {
+  const size_t T = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (; i + (U - 1) * T < n16; i += U * T) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = src[i + k * T];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc ^= v[k];
+  }
+  for (; i < n16; i += T) acc ^= src[i];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+template <int U>
+int run_stream_read(int wg_per_cu, double* out3) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  constexpr size_t kBytes = size_t(1) << 30;
+  const int blocks = cus * wg_per_cu;
+  void* buf = nullptr;
+  unsigned* out = nullptr;
+  if (hipMalloc(&buf, kBytes) != hipSuccess) return -1;
+  if (hipMalloc((void**)&out, (size_t)blocks * 256 * sizeof(unsigned)) != hipSuccess) {
+    (void)hipFree(buf);
+    return -1;
+  }
+  int rc = hipMemset(buf, 0x5a, kBytes) == hipSuccess ? 0 : -2;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (rc == 0 && (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)) rc = -2;
+  double best = 0, sum = 0;
+  const int reps = 6;
+  for (int r = 0; r < reps && rc == 0; ++r) {
+    if (hipEventRecord(e0, 0) != hipSuccess) { rc = -2; break; }
+    hipLaunchKernelGGL((stream_read_kernel<U>), dim3(blocks), dim3(256), 0, 0, (const u32x4_t*)buf, kBytes / 16, out);
+    if (hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) { rc = -2; break; }
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0) { rc = -3; break; }
+    const double gbs = (double)kBytes / (ms * 1e-3) / 1e9;
+    if (r > 0) {  // the first run warms up
+      best = std::max(best, gbs);
+      sum += gbs;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(out);
+  (void)hipFree(buf);
+  if (rc) return rc;
+  out3[0] = best;
+  out3[1] = sum / (reps - 1);
+  out3[2] = blocks;
+  return 0;
+}
+
 }  // namespace probes
 
 extern "C" {
@@ -297,6 +362,19 @@ int probe_lds(int mode, int waves_per_simd, double* out) {
     case 4: return probes::run_lds<4>(waves_per_simd, out);
     case 5: return probes::run_lds<5>(waves_per_simd, out);
     case 6: return probes::run_lds<6>(waves_per_simd, out);
+    default: return -4;
+  }
+}
+
+// Read bandwidth in GB/s (best out[0], mean out[1] of five timed passes over 1 GiB) and
+// the grid size (out[2]) of the streaming kernel with `wg_per_cu` workgroups of 256
+// threads per CU (1..8) and `in_flight` 16-byte loads per thread per iteration (1, 4, 8).
+int probe_stream_read(int wg_per_cu, int in_flight, double* out) {
+  if (!out || wg_per_cu < 1 || wg_per_cu > 8) return -4;
+  switch (in_flight) {
+    case 1: return probes::run_stream_read<1>(wg_per_cu, out);
+    case 4: return probes::run_stream_read<4>(wg_per_cu, out);
+    case 8: return probes::run_stream_read<8>(wg_per_cu, out);
     default: return -4;
   }
 }

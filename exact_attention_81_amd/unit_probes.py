@@ -2,7 +2,7 @@
 
     python -m exact_attention_81_amd.unit_probes [--json]
 
-Two questions the attention kernels' design depends on:
+Three questions the attention kernels' design depends on:
 
   * Do the hardware exponential (v_exp_f32) and the FMA (v_fma_f32) issue side by
     side? For each mix of independent exponential and FMA chains the probe reports
@@ -15,6 +15,9 @@ Two questions the attention kernels' design depends on:
     same wave, at one and two waves per SIMD; with the reads drained every 8 steps, and
     with reads kept in flight across steps (8 deep, or 4 products ahead of the
     product that uses them).
+  * How fast can a plain kernel stream reads from HBM? A grid-stride loop of 16-byte
+    loads over 1 GiB, at 1 to 8 workgroups per CU and 1 to 8 loads in flight per
+    thread: the reference for the split-KV decode, which is bound by its K/V reads.
 
 Needs a GPU; the library is built by ``build.build_probes()``.
 """
@@ -27,9 +30,11 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libexattn_probes.so")
-SYMBOLS = ("probe_exp_fma", "probe_lds")
+SYMBOLS = ("probe_exp_fma", "probe_lds", "probe_stream_read")
 
 EXP_FMA_MIXES = ((8, 0), (0, 8), (0, 16), (8, 8), (8, 16), (8, 24), (16, 16))
+STREAM_WG_PER_CU = (1, 2, 4, 8)
+STREAM_IN_FLIGHT = (1, 4, 8)
 LDS_MODES = {0: "ds_read_b128", 1: "ds_read_b64_tr_b16 x2", 2: "mfma 32x32x16 bf16 only",
              3: "mfma + ds_read_b128", 4: "mfma + ds_read_b64_tr_b16 x2",
              5: "ds_read_b128, 8 in flight", 6: "mfma fed by ds_read_b128 issued 4 ahead"}
@@ -45,6 +50,7 @@ def load() -> ctypes.CDLL:
     lib.probe_exp_fma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.POINTER(ctypes.c_double)]
     lib.probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.probe_stream_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     return lib
 
 
@@ -58,7 +64,7 @@ def _call(fn, *args):
 
 def run() -> dict:
     lib = load()
-    res = {"exp_fma": [], "lds": []}
+    res = {"exp_fma": [], "lds": [], "stream_read": []}
     for wps in (1, 2):
         for ne, nf in EXP_FMA_MIXES:
             per_instr, ghz, _ = _call(lib.probe_exp_fma, ne, nf, wps)
@@ -71,6 +77,11 @@ def run() -> dict:
                                "lds_bytes_per_clk_cu": bpc if mode != 2 else None,
                                "cycles_per_mfma": mfma_cyc if mode in (2, 3, 4, 6) else None,
                                "ghz": ghz})
+    for wpc in STREAM_WG_PER_CU:
+        for u in STREAM_IN_FLIGHT:
+            best, mean, grid = _call(lib.probe_stream_read, wpc, u)
+            res["stream_read"].append({"wg_per_cu": wpc, "in_flight": u, "best_gbs": best,
+                                       "mean_gbs": mean, "grid": int(grid)})
     return res
 
 
@@ -97,6 +108,10 @@ def report(res: dict) -> str:
         b = "" if r["lds_bytes_per_clk_cu"] is None else f"{r['lds_bytes_per_clk_cu']:.1f}"
         c = "" if r["cycles_per_mfma"] is None else f"{r['cycles_per_mfma']:.1f}"
         lines.append(f"| {r['waves_per_simd']} | {r['mode']} | {b} | {c} |")
+    lines += ["", "HBM streaming read over 1 GiB (GB/s, best and mean of five passes):", "",
+              "| workgroups per CU | loads in flight per thread | best | mean |", "|---|---|---|---|"]
+    for r in res["stream_read"]:
+        lines.append(f"| {r['wg_per_cu']} | {r['in_flight']} | {r['best_gbs']:.0f} | {r['mean_gbs']:.0f} |")
     ghz = sorted({round(r["ghz"], 2) for r in res["exp_fma"] + res["lds"]})
     lines += ["", f"shader clock during the probes: {', '.join(str(g) for g in ghz)} GHz"]
     return "\n".join(lines)
