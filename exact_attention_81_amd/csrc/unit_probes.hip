@@ -10,6 +10,11 @@
 //    ds_read_b64_tr_b16, alone and with a stream of v_mfma_f32_32x32x16_bf16 in the same
 //    wave, at one and two waves per SIMD: how fast one wave can feed its matrix core
 //    from LDS.
+//  * mfma_clock: a sustained stream of v_mfma_f32_32x32x16_bf16 on every SIMD (two
+//    waves each, four independent accumulators per wave), with operands that are
+//    constant or pseudo-random bf16 (four different operand registers in turn, so the
+//    bits on the matrix core's inputs change from product to product as with real
+//    data): the matrix rate and the shader clock the chip holds under that load.
 //  * stream_read: HBM read bandwidth of a plain streaming kernel (16-byte loads over a
 //    1 GiB buffer, grid-stride, a given number of loads in flight per thread and
 //    workgroups per CU), the reference for kernels bound by their reads, such as the
@@ -267,6 +272,48 @@ int run_lds(int waves_per_simd, double* out3) {
   return 0;
 }
 
+constexpr int kMfmaClockIter = 65536;  // 8 products each: about 17 M cycles per launch
+
+// Two pseudo-random bf16 values in one word (finite, 2^-8 <= |x| < 1): an integer hash
+// of the argument gives each half a sign, 7 mantissa bits and a biased exponent in
+// 119..126.
+__device__ inline unsigned rand_bf16x2(unsigned h) {
+  h ^= h >> 16; h *= 0x7feb352dU; h ^= h >> 15; h *= 0x846ca68bU; h ^= h >> 16;
+  const unsigned m = h & 0x807F807Fu;                         // sign, mantissa per half
+  const unsigned e = ((h >> 8) & 0x00070007u) + 0x00770077u;  // biased exponents 119..126
+  return m | (e << 7);
+}
+
+template <bool RANDOM>
+__global__ __launch_bounds__(512) void mfma_clock_kernel(float* out, long long* clk) {
+  const unsigned t = threadIdx.x + blockIdx.x * blockDim.x;
+  u32x4_t a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      a[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w) : 0x3F803F80u;      // 1.0
+      b[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w + 4u) : 0x3F003F00u;  // 0.5
+    }
+  f32x16_t c[4] = {};
+  const long long t0 = clock64(), w0 = wall_clock64();
+  for (int it = 0; it < kMfmaClockIter; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      c[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[u & 3]),
+                                                         __builtin_bit_cast(bf16x8_t, b[(u + 1) & 3]),
+                                                         c[u & 3], 0, 0, 0);
+  }
+  const long long t1 = clock64(), w1 = wall_clock64();
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += c[k][r];
+  out[t] = sum;
+  stamp(clk, t0, t1, w0, w1);
+}
+
 // Every thread reads 16-byte chunks i = tid, tid + T, ... of the buffer (T threads in
 // the grid), U chunks per loop iteration kept in flight, and folds them into one word
 // so that no load can be dropped; the folded words go to `out`.
@@ -285,6 +332,28 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   }
   for (; i < n16; i += T) acc ^= src[i];
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+template <bool RANDOM>
+int run_mfma_clock(double* out3) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  const int threads = 512;  // two waves per SIMD
+  double cyc = 0, ghz = 0;
+  // `timed` launches twice and keeps the second; four more launches first let the
+  // clock settle under the load.
+  for (int warm = 0; warm < 4; ++warm) {
+    const int rc = timed([&](float* o, long long* clk) {
+      hipLaunchKernelGGL((mfma_clock_kernel<RANDOM>), dim3(cus), dim3(threads), 0, 0, o, clk);
+    }, cus, threads, &cyc, &ghz);
+    if (rc) return rc;
+  }
+  const double products = (double)kMfmaClockIter * 8 * (threads / 64) * cus;
+  const double seconds = cyc / (ghz * 1e9);
+  out3[0] = products * 2.0 * 32 * 32 * 16 / seconds / 1e12;  // TFLOP/s
+  out3[1] = ghz;
+  out3[2] = out3[0] / (cus * 4096.0 * ghz * 1e9 / 1e12);    // of the peak at that clock
+  return 0;
 }
 
 template <int U>
@@ -364,6 +433,14 @@ int probe_lds(int mode, int waves_per_simd, double* out) {
     case 6: return probes::run_lds<6>(waves_per_simd, out);
     default: return -4;
   }
+}
+
+// bf16 MFMA stream on every SIMD: TFLOP/s (out[0]), shader clock in GHz (out[1]) and the
+// fraction of the peak at that clock (out[2]); `random_operands` 0: constant operands,
+// 1: pseudo-random bf16 operands.
+int probe_mfma_clock(int random_operands, double* out) {
+  if (!out) return -4;
+  return random_operands ? probes::run_mfma_clock<true>(out) : probes::run_mfma_clock<false>(out);
 }
 
 // Read bandwidth in GB/s (best out[0], mean out[1] of five timed passes over 1 GiB) and

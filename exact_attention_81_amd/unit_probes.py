@@ -2,7 +2,7 @@
 
     python -m exact_attention_81_amd.unit_probes [--json]
 
-Three questions the attention kernels' design depends on:
+Four questions the attention kernels' design depends on:
 
   * Do the hardware exponential (v_exp_f32) and the FMA (v_fma_f32) issue side by
     side? For each mix of independent exponential and FMA chains the probe reports
@@ -15,6 +15,9 @@ Three questions the attention kernels' design depends on:
     same wave, at one and two waves per SIMD; with the reads drained every 8 steps, and
     with reads kept in flight across steps (8 deep, or 4 products ahead of the
     product that uses them).
+  * What clock does the chip hold under a pure matrix-core load? A stream of
+    v_mfma_f32_32x32x16_bf16 on every SIMD with constant and with pseudo-random bf16
+    operands: the rate and clock the attention kernels' power budget is set against.
   * How fast can a plain kernel stream reads from HBM? A grid-stride loop of 16-byte
     loads over 1 GiB, at 1 to 8 workgroups per CU and 1 to 8 loads in flight per
     thread: the reference for the split-KV decode, which is bound by its K/V reads.
@@ -30,7 +33,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libexattn_probes.so")
-SYMBOLS = ("probe_exp_fma", "probe_lds", "probe_stream_read")
+SYMBOLS = ("probe_exp_fma", "probe_lds", "probe_stream_read", "probe_mfma_clock")
 
 EXP_FMA_MIXES = ((8, 0), (0, 8), (0, 16), (8, 8), (8, 16), (8, 24), (16, 16))
 STREAM_WG_PER_CU = (1, 2, 4, 8)
@@ -51,6 +54,7 @@ def load() -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_double)]
     lib.probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     lib.probe_stream_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.probe_mfma_clock.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     return lib
 
 
@@ -64,7 +68,7 @@ def _call(fn, *args):
 
 def run() -> dict:
     lib = load()
-    res = {"exp_fma": [], "lds": [], "stream_read": []}
+    res = {"exp_fma": [], "lds": [], "stream_read": [], "mfma_clock": []}
     for wps in (1, 2):
         for ne, nf in EXP_FMA_MIXES:
             per_instr, ghz, _ = _call(lib.probe_exp_fma, ne, nf, wps)
@@ -77,6 +81,10 @@ def run() -> dict:
                                "lds_bytes_per_clk_cu": bpc if mode != 2 else None,
                                "cycles_per_mfma": mfma_cyc if mode in (2, 3, 4, 6) else None,
                                "ghz": ghz})
+    for rnd in (0, 1):
+        tf, ghz, frac = _call(lib.probe_mfma_clock, rnd)
+        res["mfma_clock"].append({"operands": "pseudo-random bf16" if rnd else "constant",
+                                  "tflops": tf, "ghz": ghz, "of_peak_at_clock": frac})
     for wpc in STREAM_WG_PER_CU:
         for u in STREAM_IN_FLIGHT:
             best, mean, grid = _call(lib.probe_stream_read, wpc, u)
@@ -108,6 +116,10 @@ def report(res: dict) -> str:
         b = "" if r["lds_bytes_per_clk_cu"] is None else f"{r['lds_bytes_per_clk_cu']:.1f}"
         c = "" if r["cycles_per_mfma"] is None else f"{r['cycles_per_mfma']:.1f}"
         lines.append(f"| {r['waves_per_simd']} | {r['mode']} | {b} | {c} |")
+    lines += ["", "Sustained bf16 MFMA stream (v_mfma_f32_32x32x16_bf16, two waves per SIMD):", "",
+              "| operands | TFLOP/s | shader clock | of the peak at that clock |", "|---|---|---|---|"]
+    for r in res["mfma_clock"]:
+        lines.append(f"| {r['operands']} | {r['tflops']:.0f} | {r['ghz']:.2f} GHz | {100 * r['of_peak_at_clock']:.1f} % |")
     lines += ["", "HBM streaming read over 1 GiB (GB/s, best and mean of five passes):", "",
               "| workgroups per CU | loads in flight per thread | best | mean |", "|---|---|---|---|"]
     for r in res["stream_read"]:
