@@ -10,9 +10,9 @@
 //    ds_read_b64_tr_b16, alone and with a stream of v_mfma_f32_32x32x16_bf16 in the same
 //    wave, at one and two waves per SIMD: how fast one wave can feed its matrix core
 //    from LDS.
-//  * mfma_clock: a sustained stream of v_mfma_f32_32x32x16_bf16 on every SIMD (two
-//    waves each, four independent accumulators per wave), with operands that are
-//    constant or pseudo-random bf16 (four different operand registers in turn, so the
+//  * mfma_clock: a sustained stream of v_mfma_f32_32x32x16_bf16 (or of the e4m3
+//    v_mfma_f32_32x32x64_f8f6f4) on every SIMD (two waves each, four independent
+//    accumulators per wave), with operands that are constant or pseudo-random (four different operand registers in turn, so the
 //    bits on the matrix core's inputs change from product to product as with real
 //    data): the matrix rate and the shader clock the chip holds under that load.
 //  * stream_read: HBM read bandwidth of a plain streaming kernel (16-byte loads over a
@@ -284,25 +284,55 @@ __device__ inline unsigned rand_bf16x2(unsigned h) {
   return m | (e << 7);
 }
 
-template <bool RANDOM>
+// Four pseudo-random e4m3 codes in one word: sign and 3 mantissa bits from the hash,
+// exponent field 6 or 7 (values in [1/4, 1)), never a NaN code.
+__device__ inline unsigned rand_e4m3x4(unsigned h) {
+  h ^= h >> 16; h *= 0x7feb352dU; h ^= h >> 15; h *= 0x846ca68bU; h ^= h >> 16;
+  return (h & 0x8F8F8F8Fu) | 0x30303030u;
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// FP8 false: v_mfma_f32_32x32x16_bf16; true: v_mfma_f32_32x32x64_f8f6f4 on e4m3 (half
+// the iterations: each product takes twice the cycles).
+template <bool RANDOM, bool FP8>
 __global__ __launch_bounds__(512) void mfma_clock_kernel(float* out, long long* clk) {
   const unsigned t = threadIdx.x + blockIdx.x * blockDim.x;
-  u32x4_t a[4], b[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      a[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w) : 0x3F803F80u;      // 1.0
-      b[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w + 4u) : 0x3F003F00u;  // 0.5
-    }
   f32x16_t c[4] = {};
-  const long long t0 = clock64(), w0 = wall_clock64();
-  for (int it = 0; it < kMfmaClockIter; ++it) {
+  long long t0, w0;
+  if constexpr (!FP8) {
+    u32x4_t a[4], b[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      c[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[u & 3]),
-                                                         __builtin_bit_cast(bf16x8_t, b[(u + 1) & 3]),
-                                                         c[u & 3], 0, 0, 0);
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w) : 0x3F803F80u;      // 1.0
+        b[k][w] = RANDOM ? rand_bf16x2(t * 32u + k * 8u + w + 4u) : 0x3F003F00u;  // 0.5
+      }
+    t0 = clock64(); w0 = wall_clock64();
+    for (int it = 0; it < kMfmaClockIter; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[u & 3]),
+                                                           __builtin_bit_cast(bf16x8_t, b[(u + 1) & 3]),
+                                                           c[u & 3], 0, 0, 0);
+    }
+  } else {
+    i32x8_t a[4], b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        a[k][w] = (int)(RANDOM ? rand_e4m3x4(t * 64u + k * 16u + w) : 0x38383838u);      // 1.0
+        b[k][w] = (int)(RANDOM ? rand_e4m3x4(t * 64u + k * 16u + w + 8u) : 0x30303030u);  // 0.5
+      }
+    t0 = clock64(); w0 = wall_clock64();
+    for (int it = 0; it < kMfmaClockIter / 2; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u & 3], b[(u + 1) & 3], c[u & 3],
+                                                                   0, 0, 0, 0, 0, 0);
+    }
   }
   const long long t1 = clock64(), w1 = wall_clock64();
   float sum = 0.f;
@@ -334,7 +364,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
-template <bool RANDOM>
+template <bool RANDOM, bool FP8>
 int run_mfma_clock(double* out3) {
   const int cus = device_cus();
   if (cus <= 0) return -1;
@@ -344,15 +374,15 @@ int run_mfma_clock(double* out3) {
   // clock settle under the load.
   for (int warm = 0; warm < 4; ++warm) {
     const int rc = timed([&](float* o, long long* clk) {
-      hipLaunchKernelGGL((mfma_clock_kernel<RANDOM>), dim3(cus), dim3(threads), 0, 0, o, clk);
+      hipLaunchKernelGGL((mfma_clock_kernel<RANDOM, FP8>), dim3(cus), dim3(threads), 0, 0, o, clk);
     }, cus, threads, &cyc, &ghz);
     if (rc) return rc;
   }
-  const double products = (double)kMfmaClockIter * 8 * (threads / 64) * cus;
+  const double products = (double)(FP8 ? kMfmaClockIter / 2 : kMfmaClockIter) * 8 * (threads / 64) * cus;
   const double seconds = cyc / (ghz * 1e9);
-  out3[0] = products * 2.0 * 32 * 32 * 16 / seconds / 1e12;  // TFLOP/s
+  out3[0] = products * 2.0 * 32 * 32 * (FP8 ? 64 : 16) / seconds / 1e12;  // TFLOP/s
   out3[1] = ghz;
-  out3[2] = out3[0] / (cus * 4096.0 * ghz * 1e9 / 1e12);    // of the peak at that clock
+  out3[2] = out3[0] / (cus * (FP8 ? 8192.0 : 4096.0) * ghz * 1e9 / 1e12);  // of the peak at that clock
   return 0;
 }
 
@@ -435,12 +465,18 @@ int probe_lds(int mode, int waves_per_simd, double* out) {
   }
 }
 
-// bf16 MFMA stream on every SIMD: TFLOP/s (out[0]), shader clock in GHz (out[1]) and the
-// fraction of the peak at that clock (out[2]); `random_operands` 0: constant operands,
-// 1: pseudo-random bf16 operands.
-int probe_mfma_clock(int random_operands, double* out) {
+// MFMA stream on every SIMD: TFLOP/s (out[0]), shader clock in GHz (out[1]) and the
+// fraction of the peak at that clock (out[2]). `kind` 0: bf16 constant operands, 1: bf16
+// pseudo-random operands, 2: e4m3 constant, 3: e4m3 pseudo-random.
+int probe_mfma_clock(int kind, double* out) {
   if (!out) return -4;
-  return random_operands ? probes::run_mfma_clock<true>(out) : probes::run_mfma_clock<false>(out);
+  switch (kind) {
+    case 0: return probes::run_mfma_clock<false, false>(out);
+    case 1: return probes::run_mfma_clock<true, false>(out);
+    case 2: return probes::run_mfma_clock<false, true>(out);
+    case 3: return probes::run_mfma_clock<true, true>(out);
+    default: return -4;
+  }
 }
 
 // Read bandwidth in GB/s (best out[0], mean out[1] of five timed passes over 1 GiB) and

@@ -16,8 +16,9 @@ Four questions the attention kernels' design depends on:
     with reads kept in flight across steps (8 deep, or 4 products ahead of the
     product that uses them).
   * What clock does the chip hold under a pure matrix-core load? A stream of
-    v_mfma_f32_32x32x16_bf16 on every SIMD with constant and with pseudo-random bf16
-    operands: the rate and clock the attention kernels' power budget is set against.
+    v_mfma_f32_32x32x16_bf16 (or the e4m3 v_mfma_f32_32x32x64_f8f6f4) on every SIMD with
+    constant and with pseudo-random operands: the rate and clock the attention
+    kernels' power budget is set against.
   * How fast can a plain kernel stream reads from HBM? A grid-stride loop of 16-byte
     loads over 1 GiB, at 1 to 8 workgroups per CU and 1 to 8 loads in flight per
     thread: the reference for the split-KV decode, which is bound by its K/V reads.
@@ -81,10 +82,10 @@ def run() -> dict:
                                "lds_bytes_per_clk_cu": bpc if mode != 2 else None,
                                "cycles_per_mfma": mfma_cyc if mode in (2, 3, 4, 6) else None,
                                "ghz": ghz})
-    for rnd in (0, 1):
-        tf, ghz, frac = _call(lib.probe_mfma_clock, rnd)
-        res["mfma_clock"].append({"operands": "pseudo-random bf16" if rnd else "constant",
-                                  "tflops": tf, "ghz": ghz, "of_peak_at_clock": frac})
+    for kind, name in enumerate(("bf16, constant", "bf16, pseudo-random", "e4m3, constant",
+                                 "e4m3, pseudo-random")):
+        tf, ghz, frac = _call(lib.probe_mfma_clock, kind)
+        res["mfma_clock"].append({"operands": name, "tflops": tf, "ghz": ghz, "of_peak_at_clock": frac})
     for wpc in STREAM_WG_PER_CU:
         for u in STREAM_IN_FLIGHT:
             best, mean, grid = _call(lib.probe_stream_read, wpc, u)
@@ -116,7 +117,7 @@ def report(res: dict) -> str:
         b = "" if r["lds_bytes_per_clk_cu"] is None else f"{r['lds_bytes_per_clk_cu']:.1f}"
         c = "" if r["cycles_per_mfma"] is None else f"{r['cycles_per_mfma']:.1f}"
         lines.append(f"| {r['waves_per_simd']} | {r['mode']} | {b} | {c} |")
-    lines += ["", "Sustained bf16 MFMA stream (v_mfma_f32_32x32x16_bf16, two waves per SIMD):", "",
+    lines += ["", "Sustained MFMA stream (v_mfma_f32_32x32x16_bf16 / 32x32x64_f8f6f4, two waves per SIMD):", "",
               "| operands | TFLOP/s | shader clock | of the peak at that clock |", "|---|---|---|---|"]
     for r in res["mfma_clock"]:
         lines.append(f"| {r['operands']} | {r['tflops']:.0f} | {r['ghz']:.2f} GHz | {100 * r['of_peak_at_clock']:.1f} % |")
