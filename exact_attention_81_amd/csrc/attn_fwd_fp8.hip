@@ -236,6 +236,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   // exact). A wave-uniform branch around 64 multiplies in the softmax instead splits the
   // accumulators' live ranges, and the kernel spilled 56-68 B per lane around it.
   auto pv_phase = [&](auto stage, auto hook) {
+    __builtin_amdgcn_s_setprio(0);  // the matrix phase yields to the softmax wave
     const lds_u8* st = v_lds + int(stage) * V_STAGE;
     constexpr int STEPS = 4 * NKC;  // step = kc * 4 + db
     auto vread = [&](int step) {
@@ -268,6 +269,10 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
 
   auto softmax = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // The vector ALU is this kernel's busier unit: while a wave computes its softmax it
+    // gets issue priority over the SIMD's other wave, which is then in its matrix phase
+    // and needs an issue slot only every few MFMAs (+2.5 %; the opposite order -1.7 %).
+    __builtin_amdgcn_s_setprio(1);
     const int blk = (j * BLOCK_N) / F8_SBLOCK;
     // Kept positive (a zero descale or scale gives 1e-30, which moves no score by a
     // representable amount) so that a masked score of -inf gives p = 0 by itself.
