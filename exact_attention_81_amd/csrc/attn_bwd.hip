@@ -304,19 +304,16 @@ __global__ __launch_bounds__(BW_THREADS) void attn_bwd_dq_kernel(const BwdParams
   };
   tile_loop(0, j_split, PLAIN);
   tile_loop(j_split, ntiles, MASKED);
+  // dQ leaves through LDS as whole rows (stage_rows / store_rows); the barrier orders the
+  // staging writes after every wave's last tile read.
   __builtin_amdgcn_s_waitcnt(0x0070);
-  if (my_q < p.Nq) {
-    const float sc = p.scale;
-    uint8_t* og = (uint8_t*)p.dq + (qbase + my_q) * T::ROW;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2_t w = {E::pack2(dqacc[db][g * 4 + 0] * sc, dqacc[db][g * 4 + 1] * sc),
-                           E::pack2(dqacc[db][g * 4 + 2] * sc, dqacc[db][g * 4 + 3] * sc)};
-        *(u32x2_t*)(og + (db * 32 + g * 8 + half * 4) * 2) = w;
-      }
-  }
+  static_assert(BW_WAVES * 32 * staged_row_bytes<D>() <= 2 * 2 * TILE, "dQ staging fits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  lds_u8* const own = (lds_u8*)smem + wave * 32 * staged_row_bytes<D>();
+  stage_rows<D, E>(own, dqacc, p.scale, lane);
+  store_rows<D>((uint8_t*)p.dq + qbase * T::ROW, T::ROW, own, q0 + 32 * wave, p.Nq, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -385,7 +382,6 @@ __global__ __launch_bounds__(64 * KV_WAVES) void attn_bwd_dkdv_kernel(const BwdP
     for (int r = 0; r < 16; ++r) dkacc[db][r] = dvacc[db][r] = 0.f;
   TrOffsets<D> tro(lane);
   const float c = p.scale_log2;
-  const bool key_ok = my_k < p.Nkv;
 
   // One tile of the wave's 32 queries: S = Q K^T, then dP = dO V^T with P = exp2(c S -
   // LSE log2 e) computed beside those products, then dV^T += dO^T P with dS = P (dP - D)
@@ -516,28 +512,24 @@ __global__ __launch_bounds__(64 * KV_WAVES) void attn_bwd_dkdv_kernel(const BwdP
       }
   }
   wait_all_and_barrier();
-  if (qh == 0 && key_ok) {
-    const float sc = p.scale;
-    uint8_t* kgo = (uint8_t*)p.dk + (kbase + my_k) * T::ROW;
-    uint8_t* vgo = (uint8_t*)p.dv + (kbase + my_k) * T::ROW;
+  if (qh == 0) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         dkacc[db][r] += sums[((2 * db) * 16 + r) * 64 + lane];
         dvacc[db][r] += sums[((2 * db + 1) * 16 + r) * 64 + lane];
       }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int off = (db * 32 + g * 8 + half * 4) * 2;
-        const u32x2_t wk = {E::pack2(dkacc[db][g * 4 + 0] * sc, dkacc[db][g * 4 + 1] * sc),
-                            E::pack2(dkacc[db][g * 4 + 2] * sc, dkacc[db][g * 4 + 3] * sc)};
-        const u32x2_t wv = {E::pack2(dvacc[db][g * 4 + 0], dvacc[db][g * 4 + 1]),
-                            E::pack2(dvacc[db][g * 4 + 2], dvacc[db][g * 4 + 3])};
-        *(u32x2_t*)(kgo + off) = wk;
-        *(u32x2_t*)(vgo + off) = wv;
-      }
-    }
+    // dK and dV leave through LDS as whole rows (stage_rows / store_rows), staged in this
+    // wave's own partial-sum area after its last read of it (one wave: the LDS keeps the
+    // order). Rows past N_kv are not stored.
+    static_assert(2 * 32 * staged_row_bytes<D>() <= 2 * DB * 16 * 64 * 4, "dK/dV staging fits");
+    lds_u8* const own = (lds_u8*)smem + kw * (2 * DB * 16 * 64 * 4);
+    stage_rows<D, E>(own, dkacc, p.scale, lane);
+    stage_rows<D, E>(own + 32 * staged_row_bytes<D>(), dvacc, 1.f, lane);
+    store_rows<D>((uint8_t*)p.dk + kbase * T::ROW, T::ROW, own, wk0, p.Nkv, lane);
+    store_rows<D>((uint8_t*)p.dv + kbase * T::ROW, T::ROW, own + 32 * staged_row_bytes<D>(), wk0,
+                  p.Nkv, lane);
   }
 }
 

@@ -534,22 +534,22 @@ void attn_fwd_kernel(const FwdParams p) {
   const float l = sum_halves(l_part);
   const bool any = l > 0.f;
   const float inv = any ? __builtin_amdgcn_rcpf(l) : 0.f;
-  if (my_q_e < p.Nq) {
-    uint8_t* __restrict__ og =
-        STRIDED ? (uint8_t*)p.o + (b_ * p.o_sb + h_ * p.o_sh + (long long)my_q_e * p.o_sn) * 2
-                : (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q_e) * DV * 2;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t w = {E::pack2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv),
-                     E::pack2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv)};
-        *(u32x2_t*)(og + (db * 32 + g * 8 + half_e * 4) * 2) = w;
-      }
-    if (half_e == 0)
-      p.lse[(size_t)bh * p.Nq + my_q_e] =
-          any ? 0.69314718055994531f * (m_ref + __builtin_amdgcn_logf(l)) : -INFINITY;
-  }
+  // O leaves through LDS as whole rows (stage_rows / store_rows); the barrier orders the
+  // staging writes after every wave's last ring read and fill (each wave has waited for
+  // its own fills above).
+  static_assert(NWAVES * ROWS_PER_WAVE * staged_row_bytes<DV>() <= NSTAGE * (K_STAGE + V_STAGE),
+                "O staging fits in the rings");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  lds_u8* const ot = (lds_u8*)smem + wave * ROWS_PER_WAVE * staged_row_bytes<DV>();
+  stage_rows<DV, E>(ot, oacc, inv, lane_e);
+  uint8_t* const obase = STRIDED ? (uint8_t*)p.o + (b_ * p.o_sb + h_ * p.o_sh) * 2
+                                 : (uint8_t*)p.o + (size_t)bh * p.Nq * DV * 2;
+  store_rows<DV>(obase, STRIDED ? (size_t)p.o_sn * 2 : (size_t)DV * 2, ot, wq0, p.Nq, lane_e);
+  if (my_q_e < p.Nq && half_e == 0)
+    p.lse[(size_t)bh * p.Nq + my_q_e] =
+        any ? 0.69314718055994531f * (m_ref + __builtin_amdgcn_logf(l)) : -INFINITY;
 }
 
 // Dense BHND tensors run the kernel with compile-time row sizes; other strides (only

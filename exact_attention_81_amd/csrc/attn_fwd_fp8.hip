@@ -46,6 +46,7 @@
 
 #include "device.h"
 #include "fp8_ops.h"
+#include "mfma16.h"
 #include "tile_io.h"
 
 namespace exattn {
@@ -271,7 +272,7 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // The vector ALU is this kernel's busier unit: while a wave computes its softmax it
     // gets issue priority over the SIMD's other wave, which is then in its matrix phase
-    // and needs an issue slot only every few MFMAs (+2.5 %; the opposite order -1.7 %).
+    // and needs an issue slot only every few MFMAs (+2.5 %; the opposite order -1.5 %).
     __builtin_amdgcn_s_setprio(1);
     const int blk = (j * BLOCK_N) / F8_SBLOCK;
     // Kept positive (a zero descale or scale gives 1e-30, which moves no score by a
@@ -449,22 +450,20 @@ void attn_fwd_fp8_kernel(const FwdParams p) {
   const float l = l_row;
   const bool any = l > 0.f;
   const float inv = any ? dv_ref * __builtin_amdgcn_rcpf(l) : 0.f;
-  if (my_q_e < p.Nq) {
-    uint8_t* __restrict__ og = (uint8_t*)p.o + ((size_t)bh * p.Nq + my_q_e) * D * 2;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x2_t a = {oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv};
-        const f32x2_t b = {oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv};
-        u32x2_t w = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2_t)),
-                     __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2_t))};
-        *(u32x2_t*)(og + (db * 32 + g * 8 + half_e * 4) * 2) = w;
-      }
-    if (half_e == 0)
-      p.lse[(size_t)bh * p.Nq + my_q_e] =
-          any ? 0.69314718055994531f * (m_ref - F8_PBIAS + __builtin_amdgcn_logf(l)) : -INFINITY;
-  }
+  // O leaves through LDS as whole rows (stage_rows / store_rows, bf16 with round to
+  // nearest even); the barrier orders the staging writes after every wave's last ring
+  // read and fill.
+  static_assert(NWAVES * F8_ROWS * staged_row_bytes<D>() <= NSTAGE * (K_STAGE + V_STAGE),
+                "O staging fits in the rings");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  lds_u8* const ot = (lds_u8*)smem + wave * F8_ROWS * staged_row_bytes<D>();
+  stage_rows<D, Elem<false>>(ot, oacc, inv, lane_e);
+  store_rows<D>((uint8_t*)p.o + (size_t)bh * p.Nq * D * 2, D * 2, ot, wq0, p.Nq, lane_e);
+  if (my_q_e < p.Nq && half_e == 0)
+    p.lse[(size_t)bh * p.Nq + my_q_e] =
+        any ? 0.69314718055994531f * (m_ref - F8_PBIAS + __builtin_amdgcn_logf(l)) : -INFINITY;
 }
 
 }  // namespace
