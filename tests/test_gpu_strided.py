@@ -73,6 +73,27 @@ def test_padded_rows_and_packed_kv():
     compare(f64(o), f64(lse), o_ref, lse_ref, "packed kv")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_padded_output_rows_untouched(d):
+    """O written into rows padded by 8 elements, with a ragged N_q: the values match the
+    oracle and the padding, and the rows past N_q of the buffer, keep their sentinel."""
+    dev = require_gpu()
+    B, H, nq, nkv = 2, 3, 200, 333
+    q, k, v = synth.qkv(B, H, nq, nkv, d, d, seed=90 + d)
+    label = f"padded output rows d{d}"
+    log("start " + label)
+    sentinel = -7.0
+    buf = torch.full((B, H, nq + 5, d + 8), sentinel, dtype=q.dtype, device=dev)
+    out = buf[:, :, :nq, :d]
+    o, lse = ea.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=True, out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == buf.data_ptr()
+    o_ref, lse_ref = oracle.attention(q, k, v, d ** -0.5, True)
+    compare(f64(o), f64(lse), o_ref, lse_ref, label)
+    assert bool((buf[..., d:] == sentinel).all()), "row padding written"
+    assert bool((buf[:, :, nq:] == sentinel).all()), "rows past N_q written"
+
+
 def test_strided_rejects_bad_views():
     dev = require_gpu()
     q, k, v = synth.qkv(1, 2, 64, 64, 128, 128, seed=78)
